@@ -1,0 +1,120 @@
+"""CPU oracle for row-wise top-k selection -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the CPU-baseline leg of ``bench.py``
+may import this package. The GPU library never does, and nothing here is
+shared with it: the oracle is a separate C++ file (``rtopk_oracle.cpp``)
+compiled with g++ and loaded through ctypes.
+
+``exact`` is the plain definition of row-wise top-k (RTop-K summary page,
+"Problem"/"Approach"; MaxK-GNN review, "How MaxK-GNN works": exactly k
+survivors per row), ties at the k-th value going to the lowest indices.
+``capped`` is the threshold search with early stopping and tie fill of the RTop-K
+summary page, "Approach", in the reading spelled out in ``rtopk_oracle.cpp``.
+Both return the survivors of each row in ascending index order.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "rtopk_oracle.cpp")
+_LIB_PATH = os.path.join(_HERE, "librtopk_oracle.so")
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with g++ (IEEE single precision, no contraction)."""
+    cmd = [
+        "g++", "-std=c++17", "-O2", "-fopenmp", "-ffp-contract=off",
+        "-fno-fast-math", "-fPIC", "-shared", "-o", _LIB_PATH + ".tmp", _SRC,
+    ]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    f32p = ctypes.POINTER(ctypes.c_float)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.oracle_exact.argtypes = [f32p, ctypes.c_int64, ctypes.c_int32,
+                                 ctypes.c_int32, f32p, i32p]
+    lib.oracle_exact.restype = ctypes.c_int
+    lib.oracle_capped.argtypes = [f32p, ctypes.c_int64, ctypes.c_int32,
+                                  ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_float, ctypes.c_int32, f32p, i32p,
+                                  i32p, f32p, f32p]
+    lib.oracle_capped.restype = ctypes.c_int
+    lib.oracle_threads.argtypes = []
+    lib.oracle_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _as_rows(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim != 2:
+        raise ValueError("x must be a 2-D [N, M] array")
+    return x
+
+
+def _fp(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def _ip(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def exact(x, k: int):
+    """Exact top-k of every row: (values [N,k] f32, indices [N,k] i32)."""
+    x = _as_rows(x)
+    n, m = x.shape
+    vals = np.empty((n, k), dtype=np.float32)
+    idx = np.empty((n, k), dtype=np.int32)
+    rc = _load().oracle_exact(_fp(x), n, m, k, _fp(vals), _ip(idx))
+    if rc != 0:
+        raise ValueError(f"oracle_exact: invalid arguments (N={n}, M={m}, k={k})")
+    return vals, idx
+
+
+def capped(x, k: int, max_iter: int = -1, eps: float = 0.0,
+           fill_from_row_min: bool = False, return_state: bool = False):
+    """Capped threshold search with tie fill.
+
+    Returns (values, indices) or, with ``return_state``, (values, indices,
+    counts, lo, hi) where counts is the number of counts each row performed
+    and [lo, hi] its final search bounds.
+    """
+    x = _as_rows(x)
+    n, m = x.shape
+    vals = np.empty((n, k), dtype=np.float32)
+    idx = np.empty((n, k), dtype=np.int32)
+    counts = np.empty((n,), dtype=np.int32)
+    lo = np.empty((n,), dtype=np.float32)
+    hi = np.empty((n,), dtype=np.float32)
+    rc = _load().oracle_capped(_fp(x), n, m, k, int(max_iter),
+                               ctypes.c_float(eps), int(bool(fill_from_row_min)),
+                               _fp(vals), _ip(idx), _ip(counts), _fp(lo), _fp(hi))
+    if rc != 0:
+        raise ValueError(
+            f"oracle_capped: invalid arguments (N={n}, M={m}, k={k}, eps={eps})")
+    if return_state:
+        return vals, idx, counts, lo, hi
+    return vals, idx
+
+
+def threads() -> int:
+    """Threads the oracle's parallel loops use (OpenMP over rows)."""
+    return int(_load().oracle_threads())

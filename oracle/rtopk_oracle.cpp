@@ -1,0 +1,195 @@
+// CPU oracle for row-wise top-k selection.
+//
+// TEST INFRASTRUCTURE ONLY. This file is the plain, slow reference that the
+// GPU library is checked against. Only the test suite, the smoke check and the
+// CPU-baseline leg of the benchmark load it; the library never does. It shares
+// no code, header, table or helper with the GPU path.
+//
+// Two modes, one per function:
+//
+//   oracle_exact   -- the plain definition of row-wise top-k: the k largest
+//                     values of each row (RTop-K summary page, sections
+//                     "Problem" and "Approach"; MaxK-GNN review, "How MaxK-GNN
+//                     works": exactly k survivors per row). Where ties straddle
+//                     the k-th largest value, the lowest indices win. The
+//                     survivors are written in ascending index order (the pages
+//                     only ask for unsorted output).
+//
+//   oracle_capped  -- the threshold search of the RTop-K summary page, section
+//                     "Approach": bisection over the row's value range until a
+//                     threshold selects k elements, an optional cap on the
+//                     number of search steps (early stopping, sections "Key
+//                     results" and "Measured effects") and a precision epsilon
+//                     ("Surprising findings"), followed by a second pass that
+//                     fills the remaining slots from the search's lower bound.
+//                     The page gives prose only; the exact reading of each step
+//                     (midpoint formula, count predicate, stop order, fill
+//                     order) is fixed in the comments of capped_row below.
+//
+// Build: g++ -std=c++17 -O2 -fopenmp -ffp-contract=off -fPIC -shared.
+// Floating point: IEEE single precision, round to nearest even, no FMA
+// contraction, subnormals kept (no fast-math, so the x87/SSE flush bits stay
+// clear). The only rounding the search performs is its midpoint.
+//
+// Parity pins (see tests/test_oracle_*.py): exhaustive brute force on tiny
+// rows, the uncapped/exact equivalence, closed forms for max_iter = 0 and a
+// large epsilon, hand-worked examples under tests/golden/, the midpoint
+// against the once-rounded exact midpoint, and invariants on every output.
+
+#include <algorithm>
+#include <cstdint>
+#include <numeric>
+#include <vector>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+namespace {
+
+// Emit the selected index set of one row in ascending index order.
+void emit_ascending(const float* x, const std::vector<char>& chosen, int M,
+                    float* ov, int32_t* oi) {
+  int p = 0;
+  for (int j = 0; j < M; ++j) {
+    if (chosen[j]) {
+      ov[p] = x[j];
+      oi[p] = j;
+      ++p;
+    }
+  }
+}
+
+// Exact top-k of one row, straight from the definition: order the positions
+// by value, largest first, equal values by ascending position (a stable sort
+// of the positions under "greater value first"), and keep the first k.
+void exact_row(const float* x, int M, int k, float* ov, int32_t* oi) {
+  std::vector<int> order(M);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(),
+                   [x](int a, int b) { return x[a] > x[b]; });
+  std::vector<char> chosen(M, 0);
+  for (int i = 0; i < k; ++i) chosen[order[i]] = 1;
+  emit_ascending(x, chosen, M, ov, oi);
+}
+
+// The capped threshold search for one row.
+//
+// Reading of the "Approach" section used here (each choice is one the page
+// leaves open):
+//   * The search range starts as [min, max] of the row ("binary search over
+//     the value range").
+//   * One search step: stop if hi - lo <= eps (absolute width, single
+//     precision subtraction); mid = 0.5*lo + 0.5*hi (cannot overflow);
+//     stop if mid does not lie strictly inside (lo, hi); count the elements
+//     with x >= mid. A count equal to k ends the search with lo = hi = mid
+//     ("a threshold that selects k elements"); a larger count raises lo to
+//     mid, a smaller one lowers hi to mid.
+//   * max_iter caps the number of counts; max_iter < 0 means no cap.
+//   * Second pass: A = positions with x >= hi, B = positions with
+//     lo <= x < hi, both in ascending position. The survivors are the first k
+//     of A followed by B ("a second pass using the minimum to fill
+//     borderline ties", with "the minimum" read as the lower end of the
+//     search range, which starts at the row minimum and only rises).
+//   * fill_from_row_min != 0 selects the literal alternative reading in which
+//     B = positions with row_min <= x < hi (the row minimum never moves). It
+//     exists only so that the two readings can be compared on data.
+// Invariant kept by every step: #{x >= lo} >= k, and either #{x >= hi} < k or
+// hi is the row maximum. Hence |A| + |B| >= k always.
+void capped_row(const float* x, int M, int k, int max_iter, float eps,
+                int fill_from_row_min, float* ov, int32_t* oi, int32_t* counts,
+                float* lo_out, float* hi_out) {
+  float row_min = x[0];
+  float row_max = x[0];
+  for (int j = 1; j < M; ++j) {
+    if (x[j] < row_min) row_min = x[j];
+    if (x[j] > row_max) row_max = x[j];
+  }
+  float lo = row_min;
+  float hi = row_max;
+  int steps = 0;
+  while (max_iter < 0 || steps < max_iter) {
+    if (hi - lo <= eps) break;
+    const float mid = 0.5f * lo + 0.5f * hi;
+    if (!(lo < mid && mid < hi)) break;
+    int c = 0;
+    for (int j = 0; j < M; ++j) c += (x[j] >= mid) ? 1 : 0;
+    ++steps;
+    if (c == k) {
+      lo = mid;
+      hi = mid;
+      break;
+    }
+    if (c > k)
+      lo = mid;
+    else
+      hi = mid;
+  }
+
+  const float fill_lo = fill_from_row_min ? row_min : lo;
+  std::vector<char> chosen(M, 0);
+  int taken = 0;
+  for (int j = 0; j < M && taken < k; ++j) {
+    if (x[j] >= hi) {
+      chosen[j] = 1;
+      ++taken;
+    }
+  }
+  for (int j = 0; j < M && taken < k; ++j) {
+    if (!chosen[j] && x[j] >= fill_lo && x[j] < hi) {
+      chosen[j] = 1;
+      ++taken;
+    }
+  }
+  emit_ascending(x, chosen, M, ov, oi);
+  if (counts) *counts = steps;
+  if (lo_out) *lo_out = lo;
+  if (hi_out) *hi_out = hi;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Exact row-wise top-k. x is [N, M] row-major; out_val / out_idx are [N, k]
+// row-major and receive each row's k survivors in ascending index order.
+// Requires 1 <= k <= M. Returns 0 on success, 1 on invalid arguments.
+int oracle_exact(const float* x, int64_t N, int32_t M, int32_t k,
+                 float* out_val, int32_t* out_idx) {
+  if (N < 0 || M < 1 || k < 1 || k > M) return 1;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < N; ++r) {
+    exact_row(x + r * M, M, k, out_val + r * k, out_idx + r * k);
+  }
+  return 0;
+}
+
+// Capped threshold search (see capped_row). counts / lo_out / hi_out are
+// optional [N] outputs (pass NULL to skip): the number of counts performed and
+// the final search bounds of each row. Returns 0 on success, 1 on invalid
+// arguments (including eps < 0 or NaN).
+int oracle_capped(const float* x, int64_t N, int32_t M, int32_t k,
+                  int32_t max_iter, float eps, int32_t fill_from_row_min,
+                  float* out_val, int32_t* out_idx, int32_t* counts,
+                  float* lo_out, float* hi_out) {
+  if (N < 0 || M < 1 || k < 1 || k > M) return 1;
+  if (!(eps >= 0.0f)) return 1;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < N; ++r) {
+    capped_row(x + r * M, M, k, max_iter, eps, fill_from_row_min,
+               out_val + r * k, out_idx + r * k, counts ? counts + r : nullptr,
+               lo_out ? lo_out + r : nullptr, hi_out ? hi_out + r : nullptr);
+  }
+  return 0;
+}
+
+// Number of threads a parallel region of this library uses.
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+}  // extern "C"
