@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Throughput of row-wise top-k on one MI355X.
+
+Default workload (the headline): 262,144 rows x 256 fp32, exact top-32 with
+one-byte column indices (the compressed balanced layout of a MaxK
+nonlinearity), rows = N(0,1) x per-row scale U(0.5,2) with 5% exact zeros
+(workloads.py). One step = one call of the library over the whole batch.
+Inputs rotate over several resident buffers so that the 256 MB last-level
+cache cannot serve them; everything is in HBM before timing starts.
+
+Prints one JSON line: rows/s (whole job), the kernel's achieved algorithmic
+HBM bandwidth against the 8 TB/s peak (roofline), the HBM traffic measured by
+rocprofv3 counters when they match the current kernel sources, and the CPU
+oracle's throughput on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "rows/sec and achieved HBM GB/s (% of peak), N=262144 M=256 k=32 fp32"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["rtopk_rows.hpp", "rtopk_dispatch.hip", "rtopk_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "row_wise_top_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources for this workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_hash") != kernel_source_hash():
+        return None
+    return float(rec["bytes_per_launch"])
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--rows", type=int, default=262144)
+    p.add_argument("--m", type=int, default=256)
+    p.add_argument("--k", type=int, default=32)
+    p.add_argument("--mode", choices=["exact", "capped"], default="exact")
+    p.add_argument("--max-iter", type=int, default=-1)
+    p.add_argument("--eps", type=float, default=0.0)
+    p.add_argument("--index", choices=["u8", "i32"], default="u8")
+    p.add_argument("--inputs", choices=["maxk", "normal", "grid"], default="maxk")
+    p.add_argument("--buffers", type=int, default=0,
+                   help="input buffers to rotate (0: enough to exceed 768 MB)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="approximate CPU time for the oracle baseline (0: skip)")
+    p.add_argument("--copy-reference", action="store_true",
+                   help="after timing, run a plain 256 MiB device copy so that a "
+                        "counter run can calibrate FETCH_SIZE / WRITE_SIZE")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not "
+              "supported (rows are independent: a multi-GPU run would give each "
+              "GPU its own block of rows with no exchange).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import row_wise_top_amd as rt
+    import workloads
+
+    n, m, k = args.rows, args.m, args.k
+    u8 = args.index == "u8"
+    if args.inputs == "maxk":
+        x_np = workloads.maxk_activation(n, m, workloads.CONFIG_SEEDS[3])
+    elif args.inputs == "normal":
+        x_np = workloads.normal(n, m, 6)
+    else:
+        x_np = workloads.grid_ties(n, m, 5)
+    in_bytes = x_np.nbytes
+    nbuf = args.buffers or max(1, -(-768 * 2**20 // in_bytes))
+    dev = torch.device("cuda:0")
+    xs = [torch.from_numpy(x_np).to(dev)]
+    for b in range(1, nbuf):
+        # Same rows, rotated by b rows: a different byte image of the workload.
+        xs.append(torch.roll(xs[0], shifts=b, dims=0).contiguous())
+    idx_dtype = torch.uint8 if u8 else torch.int32
+    out_v = torch.empty((n, k), dtype=torch.float32, device=dev)
+    out_i = torch.empty((n, k), dtype=idx_dtype, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    if args.mode == "exact":
+        fn = rt.rtopk_select_exact_u8 if u8 else rt.rtopk_select_exact
+
+        def step(i):
+            fn(xs[i % nbuf], k, out_val=out_v, out_idx=out_i)
+    else:
+        fn = rt.rtopk_select_u8 if u8 else rt.rtopk_select
+
+        def step(i):
+            fn(xs[i % nbuf], k, args.max_iter, args.eps, out_val=out_v, out_idx=out_i)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = total_ms / args.steps
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+
+    if args.copy_reference:
+        # Plain copy of known size (268,435,456 bytes read and written).
+        src = torch.empty(2**26, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    idx_bytes = 1 if u8 else 4
+    per_row = 4 * m + k * (4 + idx_bytes)
+    algo_bytes = n * per_row
+    achieved = algo_bytes / (avg_launch_ms * 1e-3) / 1e9
+    workload = (f"{args.inputs} N={n} M={m} k={k} {args.mode}"
+                + ("" if args.mode == "exact" else f" max_iter={args.max_iter} eps={args.eps}")
+                + f" idx={args.index}")
+    traffic = measured_traffic(workload)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        oracle.exact(x_np[:1024], k)  # load and warm
+        passes, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds and passes < 100:
+            t = time.perf_counter()
+            if args.mode == "exact":
+                oracle.exact(x_np, k)
+            else:
+                oracle.capped(x_np, k, args.max_iter, args.eps)
+            t_cpu += time.perf_counter() - t
+            passes += 1
+        cpu = {"value": passes * n / t_cpu, "unit": "rows/s",
+               "cores": oracle.threads(), "kind": "oracle",
+               "sample": f"{passes} full pass(es) over the same {n}-row batch "
+                         f"({t_cpu:.1f} s of oracle time)"}
+
+    line = {
+        "metric": METRIC,
+        "value": n / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": workload, "rows": n, "row_length": m, "k": k,
+                   "mode": args.mode, "index": args.index,
+                   "input_buffers": nbuf, "bytes_per_row": per_row},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "kernel_avg_us": avg_launch_ms * 1e3,
+        "kernel_min_us": min(launch_ms) * 1e3,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,114 @@
+/*
+ * rtopk.h -- C ABI of the row-wise top-k library for MI355X (gfx950).
+ *
+ * Operation. For every row of a row-major [N, M] single-precision matrix,
+ * select k of its M elements and write them, unsorted by value, as two dense
+ * row-major [N, k] arrays: the selected values and their column indices. This
+ * is the row-wise top-k of the RTop-K summary page ("RTop-K: Ultra-Fast
+ * Row-Wise Top-K Selection for Neural Network Acceleration on GPUs", sections
+ * "Problem" and "Approach"), whose output is the two-array compressed
+ * balanced layout (data + index, exactly k per row) of the MaxK-GNN review
+ * ("MaxK-GNN: Extremely Fast GPU Kernel Design ...", section "How MaxK-GNN
+ * works") and the MaxK-GNN abstract (CBSR format).
+ *
+ * Output order. Within a row the k survivors are listed in ascending column
+ * index. Both the exact and the capped entry points write exactly k entries
+ * per row; out_idx[r*k + i] is a distinct column in [0, M) and
+ * out_val[r*k + i] is bitwise x[r*M + out_idx[r*k + i]].
+ *
+ * Arguments common to every entry point.
+ *   x        device pointer to N*M floats, row r at x + r*M (no padding).
+ *            Elements must be finite; NaN or infinity gives an unspecified
+ *            (but in-bounds) selection. -0.0 and +0.0 compare equal.
+ *   N        number of rows, N >= 0. N == 0 returns RTOPK_SUCCESS and
+ *            launches nothing. 64-bit: inputs beyond 4 GiB are supported.
+ *   M        row length, 1 <= M <= RTOPK_MAX_ROW_LENGTH (8192; the summary
+ *            page, "Limitations", reports the method unsupported beyond it).
+ *   k        survivors per row, 1 <= k <= M.
+ *   out_val  device pointer to N*k floats, written.
+ *   out_idx  device pointer to N*k indices (int32, or uint8 for the _u8
+ *            forms), written.
+ *   stream   HIP stream to enqueue on; NULL means the null stream.
+ * Outputs must not overlap x or each other. All pointers are owned by the
+ * caller; the library allocates, frees and synchronises nothing, and keeps no
+ * state between calls apart from cached device properties (re-entrant).
+ *
+ * Asynchrony. Each call validates its arguments on the host, enqueues one
+ * kernel on `stream` and returns. Faults in the kernel surface at the
+ * caller's next synchronisation, as for any HIP launch.
+ *
+ * Errors. RTOPK_ERROR_INVALID_VALUE: a NULL pointer (when N > 0), N < 0,
+ * M < 1, k < 1, k > M, eps < 0 or NaN. RTOPK_ERROR_NOT_SUPPORTED:
+ * M > RTOPK_MAX_ROW_LENGTH, or a _u8 form with M > 256. RTOPK_ERROR_LAUNCH:
+ * the HIP runtime reported an error while enqueuing. On any error nothing is
+ * enqueued and the outputs are untouched.
+ */
+#ifndef RTOPK_H_
+#define RTOPK_H_
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RTOPK_MAX_ROW_LENGTH 8192
+
+typedef enum rtopk_status_t {
+  RTOPK_SUCCESS = 0,
+  RTOPK_ERROR_INVALID_VALUE = 1,
+  RTOPK_ERROR_NOT_SUPPORTED = 2,
+  RTOPK_ERROR_LAUNCH = 3
+} rtopk_status_t;
+
+/*
+ * Capped threshold search with tie fill (RTop-K summary page, "Approach";
+ * early stopping in "Key results"; precision epsilon in "Surprising
+ * findings"). Per row, in IEEE single precision with round-to-nearest-even:
+ *   lo = min(row), hi = max(row), steps = 0
+ *   while (max_iter < 0 || steps < max_iter):
+ *     if (hi - lo <= eps) stop
+ *     mid = 0.5f*lo + 0.5f*hi;  if !(lo < mid < hi) stop
+ *     c = #{x >= mid}; steps += 1
+ *     c == k: lo = hi = mid, stop;  c > k: lo = mid;  c < k: hi = mid
+ *   survivors = first k (by index) of A = {x >= hi}, then of B = {lo <= x < hi}
+ * max_iter < 0 means no cap; max_iter == 0 performs no count. eps is an
+ * absolute width (eps >= 0). With max_iter < 0 and eps == 0 the result is the
+ * exact top-k with ties at the k-th value broken by lowest index.
+ */
+rtopk_status_t rtopk_select(const float* x, int64_t N, int32_t M, int32_t k,
+                            int32_t max_iter, float eps, float* out_val,
+                            int32_t* out_idx, hipStream_t stream);
+
+/*
+ * Exact top-k (RTop-K summary page, "Problem": the k largest of each row),
+ * without sorting: the threshold search runs until it isolates the k-th
+ * largest value exactly, with a bounded number of counts per row. Ties at the
+ * k-th value go to the lowest indices, so the result equals the first k
+ * positions of a stable descending sort, re-listed by ascending index.
+ */
+rtopk_status_t rtopk_select_exact(const float* x, int64_t N, int32_t M,
+                                  int32_t k, float* out_val, int32_t* out_idx,
+                                  hipStream_t stream);
+
+/* As rtopk_select with one-byte column indices (the compressed balanced
+ * layout's index array for rows of at most 256 features). Requires M <= 256. */
+rtopk_status_t rtopk_select_u8(const float* x, int64_t N, int32_t M, int32_t k,
+                               int32_t max_iter, float eps, float* out_val,
+                               uint8_t* out_idx, hipStream_t stream);
+
+/* As rtopk_select_exact with one-byte column indices. Requires M <= 256. */
+rtopk_status_t rtopk_select_exact_u8(const float* x, int64_t N, int32_t M,
+                                     int32_t k, float* out_val,
+                                     uint8_t* out_idx, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* rtopk_status_string(rtopk_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RTOPK_H_ */

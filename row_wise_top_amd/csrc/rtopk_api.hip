@@ -1,0 +1,84 @@
+// C ABI of the row-wise top-k library: argument validation and dispatch.
+// The operation and the argument contract are documented in include/rtopk.h.
+
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "rtopk.h"
+#include "rtopk_internal.h"
+
+namespace {
+
+rtopk_status_t validate(const float* x, int64_t n, int32_t m, int32_t k,
+                        float eps, const float* out_val, const void* out_idx,
+                        bool u8_index) {
+  if (n < 0 || m < 1 || k < 1 || k > m) return RTOPK_ERROR_INVALID_VALUE;
+  if (!(eps >= 0.0f)) return RTOPK_ERROR_INVALID_VALUE;  // rejects NaN too
+  if (m > rtopk::kMaxRowLength) return RTOPK_ERROR_NOT_SUPPORTED;
+  if (u8_index && m > 256) return RTOPK_ERROR_NOT_SUPPORTED;
+  if (n > 0 && (x == nullptr || out_val == nullptr || out_idx == nullptr))
+    return RTOPK_ERROR_INVALID_VALUE;
+  return RTOPK_SUCCESS;
+}
+
+rtopk_status_t run(const float* x, int64_t n, int32_t m, int32_t k,
+                   int32_t max_iter, float eps, float* out_val, void* out_idx,
+                   bool u8_index, rtopk::Mode mode, hipStream_t stream) {
+  const rtopk_status_t st =
+      validate(x, n, m, k, eps, out_val, out_idx, u8_index);
+  if (st != RTOPK_SUCCESS) return st;
+  if (n == 0) return RTOPK_SUCCESS;
+  rtopk::SelectArgs a{x, n, m, k, max_iter, eps, out_val, out_idx, 0.0f, 0.0f, 0.0f};
+  const hipError_t err = rtopk::launch_select(a, mode, u8_index, stream);
+  return err == hipSuccess ? RTOPK_SUCCESS : RTOPK_ERROR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+rtopk_status_t rtopk_select(const float* x, int64_t N, int32_t M, int32_t k,
+                            int32_t max_iter, float eps, float* out_val,
+                            int32_t* out_idx, hipStream_t stream) {
+  return run(x, N, M, k, max_iter, eps, out_val, out_idx, false,
+             rtopk::Mode::kCapped, stream);
+}
+
+rtopk_status_t rtopk_select_exact(const float* x, int64_t N, int32_t M,
+                                  int32_t k, float* out_val, int32_t* out_idx,
+                                  hipStream_t stream) {
+  return run(x, N, M, k, -1, 0.0f, out_val, out_idx, false,
+             rtopk::Mode::kExact, stream);
+}
+
+rtopk_status_t rtopk_select_u8(const float* x, int64_t N, int32_t M, int32_t k,
+                               int32_t max_iter, float eps, float* out_val,
+                               uint8_t* out_idx, hipStream_t stream) {
+  return run(x, N, M, k, max_iter, eps, out_val, out_idx, true,
+             rtopk::Mode::kCapped, stream);
+}
+
+rtopk_status_t rtopk_select_exact_u8(const float* x, int64_t N, int32_t M,
+                                     int32_t k, float* out_val,
+                                     uint8_t* out_idx, hipStream_t stream) {
+  return run(x, N, M, k, -1, 0.0f, out_val, out_idx, true,
+             rtopk::Mode::kExact, stream);
+}
+
+const char* rtopk_status_string(rtopk_status_t status) {
+  switch (status) {
+    case RTOPK_SUCCESS:
+      return "success";
+    case RTOPK_ERROR_INVALID_VALUE:
+      return "invalid value: null pointer, N < 0, M < 1, k < 1, k > M, or eps < 0 / NaN";
+    case RTOPK_ERROR_NOT_SUPPORTED:
+      return "not supported: M > 8192, or one-byte indices with M > 256";
+    case RTOPK_ERROR_LAUNCH:
+      return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

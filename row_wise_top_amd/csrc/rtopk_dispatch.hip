@@ -1,0 +1,140 @@
+// Host-side dispatch of the row kernels: picks the kernel for the row length,
+// sizes a persistent grid to the device's resident capacity, and enqueues it.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+#include <mutex>
+#include <unordered_map>
+
+#include "rtopk_internal.h"
+
+namespace rtopk {
+namespace {
+
+// Resident blocks per CU for a kernel on a device, cached per device.
+int resident_blocks(const void* fn, int device) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, int> cache[64];
+  std::lock_guard<std::mutex> lock(mu);
+  auto& c = cache[device & 63];
+  auto it = c.find(fn);
+  if (it != c.end()) return it->second;
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, kBlock, 0) !=
+          hipSuccess ||
+      blocks < 1)
+    blocks = 1;
+  c.emplace(fn, blocks);
+  return blocks;
+}
+
+int cu_count(int device) {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  std::lock_guard<std::mutex> lock(mu);
+  int& c = cached[device & 63];
+  if (c == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount,
+                              device) != hipSuccess ||
+        v < 1)
+      v = 1;
+    c = v;
+  }
+  return c;
+}
+
+int slot_bucket(int m) {
+  const int slots = (m + kWave - 1) / kWave;
+  for (int b : kSlotBuckets) {
+    if (b >= slots) return b;
+  }
+  return 0;
+}
+
+RowsKernel kernel_for(int m, Mode mode, bool u8_index, int qc) {
+  const int q = slot_bucket(m);
+  const bool full = (m == q * kWave);
+  switch (q) {
+    case 1: return rows_kernel<1>(full, mode, u8_index, qc);
+    case 2: return rows_kernel<2>(full, mode, u8_index, qc);
+    case 3: return rows_kernel<3>(full, mode, u8_index, qc);
+    case 4: return rows_kernel<4>(full, mode, u8_index, qc);
+    case 6: return rows_kernel<6>(full, mode, u8_index, qc);
+    case 8: return rows_kernel<8>(full, mode, u8_index, qc);
+    case 12: return rows_kernel<12>(full, mode, u8_index, qc);
+    case 16: return rows_kernel<16>(full, mode, u8_index, qc);
+    case 24: return rows_kernel<24>(full, mode, u8_index, qc);
+    case 32: return rows_kernel<32>(full, mode, u8_index, qc);
+    case 48: return rows_kernel<48>(full, mode, u8_index, qc);
+    case 64: return rows_kernel<64>(full, mode, u8_index, qc);
+    case 96: return rows_kernel<96>(full, mode, u8_index, qc);
+    case 128: return rows_kernel<128>(full, mode, u8_index, qc);
+    default: return nullptr;
+  }
+}
+
+// Upper-tail quantile of the standard normal: z with P(Z > z) = p.
+double normal_upper_quantile(double p) {
+  double lo = -9.0, hi = 9.0;
+  for (int i = 0; i < 80; ++i) {
+    const double mid = 0.5 * (lo + hi);
+    if (0.5 * std::erfc(mid / std::sqrt(2.0)) > p)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+double normal_density(double z) {
+  return std::exp(-0.5 * z * z) / std::sqrt(2.0 * 3.14159265358979323846);
+}
+
+// Normal-model steering of the exact search (see rtopk_rows.hpp): the first
+// threshold aims at the middle of (k, 64*qc] elements (or k + 1/2 without
+// compaction); Newton steps use the density at the k-th largest value.
+void exact_model(SelectArgs& a, int qc) {
+  const double m = a.m;
+  const double clamp_lo = 0.5 / m, clamp_hi = 1.0 - 0.5 / m;
+  auto frac = [&](double count) {
+    return std::fmin(std::fmax(count / m, clamp_lo), clamp_hi);
+  };
+  const double first = qc > 0 ? 0.5 * (a.k + kWave * qc) : a.k + 0.5;
+  const double z_first = normal_upper_quantile(frac(first));
+  const double z_k = normal_upper_quantile(frac(a.k + 0.5));
+  a.inv_m = static_cast<float>(1.0 / m);
+  a.z_first = static_cast<float>(z_first);
+  a.half_step_per_sd = static_cast<float>(0.5 / (m * normal_density(z_k)));
+}
+
+}  // namespace
+
+hipError_t launch_select(const SelectArgs& args, Mode mode, bool u8_index,
+                         hipStream_t stream) {
+  SelectArgs a = args;
+  int qc = 0;
+  if (mode == Mode::kExact) {
+    qc = candidate_slots(slot_bucket(a.m), a.k);
+    exact_model(a, qc);
+  }
+  const RowsKernel fn = kernel_for(a.m, mode, u8_index, qc);
+  if (fn == nullptr) return hipErrorInvalidValue;
+  int device = 0;
+  hipError_t err = hipGetDevice(&device);
+  if (err != hipSuccess) return err;
+  // One wave per row at a time; a persistent grid of what fits on the device
+  // at once, each wave striding over the rows.
+  const int64_t blocks_needed = (a.n + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t resident =
+      static_cast<int64_t>(cu_count(device)) *
+      resident_blocks(reinterpret_cast<const void*>(fn), device);
+  const int64_t grid = blocks_needed < resident ? blocks_needed : resident;
+  hipLaunchKernelGGL(fn, dim3(static_cast<uint32_t>(grid)), dim3(kBlock), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace rtopk

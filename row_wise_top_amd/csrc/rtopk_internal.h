@@ -1,0 +1,62 @@
+// Internal interface between the C ABI (rtopk_api.hip) and the kernels
+// (rtopk_kernels.hip). Not installed; not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace rtopk {
+
+// Largest row length the one-wave-per-row kernels hold in registers.
+constexpr int kMaxRowLength = 8192;
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = kWave * kWavesPerBlock;
+
+enum class Mode { kCapped, kExact };
+
+struct SelectArgs {
+  const float* x;
+  int64_t n;
+  int32_t m;
+  int32_t k;
+  int32_t max_iter;  // capped mode only; < 0 = no cap
+  float eps;         // capped mode only; >= 0
+  float* out_val;
+  void* out_idx;     // int32_t* or uint8_t*
+  // Exact search only: thresholds from a normal model of the row (host
+  // computed; they steer the search, never its result).
+  float inv_m;             // 1 / m
+  float z_first;           // first threshold = mean + z_first * sd
+  float half_step_per_sd;  // Newton step per doubled count, in units of sd
+};
+
+using RowsKernel = void (*)(SelectArgs);
+
+// Slot counts Q (elements per lane) with an instantiated register-resident
+// row kernel; a row of length m uses the smallest Q with 64*Q >= m.
+constexpr int kSlotBuckets[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128};
+
+// Defined in rtopk_rows.hpp, instantiated in the rtopk_rows_*.hip units.
+// qc: candidate slots of the exact search (0: no compaction).
+template <int Q>
+RowsKernel rows_kernel(bool full, Mode mode, bool u8_index, int qc);
+
+// Candidate slots QC the exact search compacts into for q slots and k
+// survivors: the smallest of 1, 2, 4, 8 with 64*QC >= 2k and 2*QC <= q, or 0
+// when there is none (the search then stays on the whole row).
+inline int candidate_slots(int q, int k) {
+  for (int qc : {1, 2, 4, 8}) {
+    if (kWave * qc >= 2 * k && 2 * qc <= q) return qc;
+  }
+  return 0;
+}
+
+// Enqueue the selection kernel for `a` on `stream`. Arguments are already
+// validated (1 <= k <= m <= kMaxRowLength, n > 0, u8 only with m <= 256).
+// Returns the HIP error of the launch.
+hipError_t launch_select(const SelectArgs& a, Mode mode, bool u8_index,
+                         hipStream_t stream);
+
+}  // namespace rtopk

@@ -1,0 +1,682 @@
+#pragma once
+
+// Row-wise top-k kernels for gfx950 (CDNA4, wave64): device templates.
+// Included by the rtopk_rows_*.hip units, each of which instantiates the
+// kernels for a few slot counts (so the units compile in parallel).
+//
+// Method: RTop-K summary page ("RTop-K: Ultra-Fast Row-Wise Top-K Selection
+// for Neural Network Acceleration on GPUs"), section "Approach": per row, a
+// search over the value range for a threshold that selects k elements, an
+// optional cap on the number of search steps, and a second pass that fills
+// the remaining slots from the lower end of the search range. The output is
+// the two dense [N, k] arrays (values, column indices) of the compressed
+// balanced layout in the MaxK-GNN review, "How MaxK-GNN works".
+//
+// Mapping. One wave64 owns one row at a time. The row lives in registers:
+// lane l, slot s holds column 64*s + l, so each slot is one fully coalesced
+// 256-byte load and the order of columns is (slot, lane). A count of
+// elements >= t is one v_cmp per slot producing a 64-bit lane mask, summed
+// with scalar popcounts; nothing is re-read from memory during the search.
+// Compaction in column order needs only the scalar prefix over earlier slots
+// plus the lane's rank inside its slot's mask (mbcnt).
+//
+// Each wave walks rows with a grid stride and issues the loads of its next
+// row before working on the current one, so HBM reads overlap the search.
+//
+// Two searches share this skeleton:
+//  * capped (rtopk_select): the bisection of the summary page, step for step
+//    as specified in rtopk.h, from [min, max] of the row;
+//  * exact (rtopk_select_exact): any sequence of thresholds is allowed as
+//    long as the result is the exact top-k, so the thresholds are chosen to
+//    need few counts. The first one comes from the row's mean and standard
+//    deviation under a normal model, aimed at a count a little above k. Once
+//    a count lands in (k, W] (W = 64*QC), the elements at or above that
+//    threshold are the only candidates left; they are compacted through LDS
+//    into QC slots in column order, so every further count costs QC compares
+//    instead of Q. Newton steps with the model's density follow, then a
+//    "snap" to the largest candidate below the upper bound resolves ties.
+//    Bisection of the integer order keys (at most 32 counts) bounds every
+//    case the model handles badly. The model only picks thresholds; the
+//    result never depends on it.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rtopk_internal.h"
+
+namespace rtopk {
+namespace rows_detail {
+
+constexpr float kInf = __builtin_inff();
+
+// ---------------------------------------------------------------------------
+// Wave-level primitives
+// ---------------------------------------------------------------------------
+
+// Number of set bits of `mask` at lanes below the calling lane, plus `acc`.
+__device__ __forceinline__ uint32_t rank_below(uint64_t mask, uint32_t acc = 0u) {
+  return __builtin_amdgcn_mbcnt_hi(
+      static_cast<uint32_t>(mask >> 32),
+      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), acc));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) {
+  return __builtin_amdgcn_ballot_w64(p);
+}
+
+__device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
+
+// Cross-lane read through DPP, all rows and banks enabled. A lane whose
+// source does not exist (row 0 for the row broadcasts) reads 0 (bound_ctrl);
+// the reductions below only use lane 63, whose sources always exist.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                         0xf, 0xf, true));
+}
+
+// DPP controls (gfx9 encoding).
+constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+constexpr int kRowBcast15 = 0x142;    // lane 15 of each row -> next row
+constexpr int kRowBcast31 = 0x143;    // lane 31 -> rows 2 and 3
+
+__device__ __forceinline__ float lane63(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Two wave-wide reductions, interleaved so that each DPP step of one hides
+// the read-after-write wait of the other. Op is min, max or +. After the
+// four in-row steps every lane holds its row's result; the two broadcasts
+// then accumulate rows 0..3 into lane 63.
+struct OpMin {
+  __device__ static float f(float a, float b) { return fminf(a, b); }
+};
+struct OpMax {
+  __device__ static float f(float a, float b) { return fmaxf(a, b); }
+};
+struct OpAdd {
+  __device__ static float f(float a, float b) { return a + b; }
+};
+
+template <class A, class B>
+__device__ __forceinline__ void wave_reduce2(float& a, float& b) {
+  a = A::f(a, dpp<kQuadSwap1>(a));
+  b = B::f(b, dpp<kQuadSwap1>(b));
+  a = A::f(a, dpp<kQuadSwap2>(a));
+  b = B::f(b, dpp<kQuadSwap2>(b));
+  a = A::f(a, dpp<kRowHalfMirror>(a));
+  b = B::f(b, dpp<kRowHalfMirror>(b));
+  a = A::f(a, dpp<kRowMirror>(a));
+  b = B::f(b, dpp<kRowMirror>(b));
+  a = A::f(a, dpp<kRowBcast15>(a));
+  b = B::f(b, dpp<kRowBcast15>(b));
+  a = A::f(a, dpp<kRowBcast31>(a));
+  b = B::f(b, dpp<kRowBcast31>(b));
+  a = lane63(a);
+  b = lane63(b);
+}
+
+__device__ __forceinline__ float wave_max(float a) {
+  a = fmaxf(a, dpp<kQuadSwap1>(a));
+  a = fmaxf(a, dpp<kQuadSwap2>(a));
+  a = fmaxf(a, dpp<kRowHalfMirror>(a));
+  a = fmaxf(a, dpp<kRowMirror>(a));
+  a = fmaxf(a, dpp<kRowBcast15>(a));
+  a = fmaxf(a, dpp<kRowBcast31>(a));
+  return lane63(a);
+}
+
+// ---------------------------------------------------------------------------
+// Row in registers
+// ---------------------------------------------------------------------------
+
+// Load a row into slots. FULL: the row length is exactly 64*Q. Otherwise
+// lanes past the end re-read the last element (always in bounds) so that the
+// loads stay unconditional; mask_tail() then replaces them.
+template <int Q, bool FULL>
+__device__ __forceinline__ void load_row(const float* __restrict__ row, int m,
+                                         int lane, float (&v)[Q]) {
+#pragma unroll
+  for (int s = 0; s < Q; ++s) {
+    int j = s * kWave + lane;
+    if (!FULL) j = min(j, m - 1);
+    v[s] = row[j];
+  }
+}
+
+// Whether slot s of this lane holds a column of the row.
+template <bool FULL>
+__device__ __forceinline__ bool in_row(int s, int m, int lane) {
+  return FULL || s * kWave + lane < m;
+}
+
+// Positions past the end become -inf: no count and no selection test picks
+// them (every threshold used is finite or the bracket end +-inf, and the
+// tests are x >= t with t > -inf).
+template <int Q, bool FULL>
+__device__ __forceinline__ void mask_tail(int m, int lane, float (&v)[Q]) {
+  if (FULL) return;
+#pragma unroll
+  for (int s = 0; s < Q; ++s) {
+    if (!in_row<FULL>(s, m, lane)) v[s] = -kInf;
+  }
+}
+
+// #{elements >= t}: one compare per slot, scalar popcounts.
+template <int S>
+__device__ __forceinline__ int count_ge(const float (&v)[S], float t) {
+  int c = 0;
+#pragma unroll
+  for (int s = 0; s < S; ++s) c += popc(ballot(v[s] >= t));
+  return c;
+}
+
+// Order-preserving map from floats to int32 (-0 and +0 both map to 0,
+// +-inf map to +-0x7f800000) and its inverse.
+__device__ __forceinline__ int32_t order_key(float f) {
+  const int32_t b = __float_as_int(f);
+  return b >= 0 ? b : static_cast<int32_t>(0x80000000u - static_cast<uint32_t>(b));
+}
+
+__device__ __forceinline__ float key_value(int32_t key) {
+  const uint32_t b = key >= 0 ? static_cast<uint32_t>(key)
+                              : 0x80000000u - static_cast<uint32_t>(key);
+  return __int_as_float(static_cast<int32_t>(b));
+}
+
+// ---------------------------------------------------------------------------
+// Emission. Both write exactly k entries, in column order.
+// `col(s)` gives the column held by slot s of the calling lane.
+// ---------------------------------------------------------------------------
+
+// Every element >= t; the caller has counted exactly k of them.
+template <int S, typename IdxT, typename ColFn>
+__device__ __forceinline__ void emit_at_threshold(const float (&v)[S],
+                                                  ColFn col, float t,
+                                                  float* __restrict__ ov,
+                                                  IdxT* __restrict__ oi) {
+  uint32_t base = 0;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const bool p = v[s] >= t;
+    const uint64_t msk = ballot(p);
+    if (p) {
+      const uint32_t pos = rank_below(msk, base);
+      ov[pos] = v[s];
+      oi[pos] = static_cast<IdxT>(col(s));
+    }
+    base += popc(msk);
+  }
+}
+
+// The second pass: the first k (by column) of A = {x >= hi}, then of
+// B = {lo <= x < hi}. Requires #{x >= lo} >= k.
+template <int S, typename IdxT, typename ColFn>
+__device__ __forceinline__ void emit_fill(const float (&v)[S], ColFn col,
+                                          float lo, float hi, int k,
+                                          float* __restrict__ ov,
+                                          IdxT* __restrict__ oi) {
+  int nA = 0;
+#pragma unroll
+  for (int s = 0; s < S; ++s) nA += popc(ballot(v[s] >= hi));
+  const int takeA = min(nA, k);
+  const int needB = k - takeA;
+  int accA = 0, accB = 0;
+  uint32_t base = 0;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const bool a = v[s] >= hi;
+    const uint64_t mA = ballot(a);
+    const int pa = popc(mA);
+    bool selA;
+    if (accA + pa <= takeA)
+      selA = a;
+    else if (accA >= takeA)
+      selA = false;
+    else
+      selA = a && static_cast<int>(rank_below(mA, accA)) < takeA;
+    accA += pa;
+    bool selB = false;
+    if (accB < needB) {
+      const bool b = !a && (v[s] >= lo);
+      const uint64_t mB = ballot(b);
+      const int pb = popc(mB);
+      if (accB + pb <= needB)
+        selB = b;
+      else
+        selB = b && static_cast<int>(rank_below(mB, accB)) < needB;
+      accB += pb;
+    }
+    const bool sel = selA || selB;
+    const uint64_t mS = ballot(sel);
+    if (sel) {
+      const uint32_t pos = rank_below(mS, base);
+      ov[pos] = v[s];
+      oi[pos] = static_cast<IdxT>(col(s));
+    }
+    base += popc(mS);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Capped search (rtopk_select): the specification in rtopk.h, step for step.
+// Invariant: #{x >= lo} >= k and (#{x >= hi} < k or hi == row max).
+// ---------------------------------------------------------------------------
+template <int Q, bool FULL, typename IdxT>
+__device__ __forceinline__ void capped_row(const float (&vin)[Q],
+                                           const SelectArgs& a, int lane,
+                                           float* __restrict__ ov,
+                                           IdxT* __restrict__ oi) {
+  float v[Q];
+  float mn = kInf, mx = -kInf;
+#pragma unroll
+  for (int s = 0; s < Q; ++s) {
+    v[s] = vin[s];
+    mn = fminf(mn, v[s]);  // re-read tail lanes hold a real element
+    mx = fmaxf(mx, v[s]);
+  }
+  wave_reduce2<OpMin, OpMax>(mn, mx);
+  mask_tail<Q, FULL>(a.m, lane, v);
+  float lo = mn, hi = mx;
+  const int k = a.k;
+  int steps = 0;
+  while (a.max_iter < 0 || steps < a.max_iter) {
+    if (hi - lo <= a.eps) break;
+    const float mid = 0.5f * lo + 0.5f * hi;
+    if (!(lo < mid && mid < hi)) break;
+    const int c = count_ge(v, mid);
+    ++steps;
+    if (c == k) {
+      lo = mid;
+      hi = mid;
+      break;
+    }
+    // Value selects, not a branch: keeps lo/hi in scalar registers.
+    const bool up = c > k;
+    lo = up ? mid : lo;
+    hi = up ? hi : mid;
+  }
+  emit_fill(v, [lane](int s) { return s * kWave + lane; }, lo, hi, k, ov, oi);
+}
+
+// ---------------------------------------------------------------------------
+// Exact search (rtopk_select_exact).
+// Bracket invariant: #{x >= lo} = clo >= k > chi = #{x >= hi}, with
+// lo = -inf and hi = +inf allowed at the start. Every count at a threshold t
+// gives a valid new bound whether or not t lies inside the bracket (c > k:
+// lo = t; c < k: hi = t), so the pivots need no bounds check. A count of
+// exactly k at t ends the search (the result is {x >= t}); otherwise the
+// search ends on the k-th largest value v, and the result is {x > v} plus the
+// lowest columns holding v.
+// ---------------------------------------------------------------------------
+
+// Full-row Newton steps before the order-key bisection takes over.
+constexpr int kRowSteps = 4;
+// Newton steps, then snaps, on the compacted candidates.
+constexpr int kCandSteps = 6;
+constexpr int kCandSnaps = 4;
+
+__device__ __forceinline__ float wave_min(float a) {
+  a = fminf(a, dpp<kQuadSwap1>(a));
+  a = fminf(a, dpp<kQuadSwap2>(a));
+  a = fminf(a, dpp<kRowHalfMirror>(a));
+  a = fminf(a, dpp<kRowMirror>(a));
+  a = fminf(a, dpp<kRowBcast15>(a));
+  a = fminf(a, dpp<kRowBcast31>(a));
+  return lane63(a);
+}
+
+__device__ __forceinline__ float wave_sum(float a) {
+  a += dpp<kQuadSwap1>(a);
+  a += dpp<kQuadSwap2>(a);
+  a += dpp<kRowHalfMirror>(a);
+  a += dpp<kRowMirror>(a);
+  a += dpp<kRowBcast15>(a);
+  a += dpp<kRowBcast31>(a);
+  return lane63(a);
+}
+
+// The float right after f in the order of order_key.
+__device__ __forceinline__ float next_float(float f) {
+  return key_value(order_key(f) + 1);
+}
+
+// Every element >= t (the caller has counted exactly k), in column order.
+// The lane masks come straight from the compares, so the stores run under
+// exec = mask without re-deriving the predicate.
+template <int S, typename IdxT, typename ColFn>
+__device__ __forceinline__ void emit_ge(const float (&v)[S], ColFn col,
+                                        float t, float* __restrict__ ov,
+                                        IdxT* __restrict__ oi) {
+  uint32_t base = 0;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const uint64_t msk = ballot(v[s] >= t);
+    if (__builtin_amdgcn_inverse_ballot_w64(msk)) {
+      const uint32_t pos = rank_below(msk, base);
+      ov[pos] = v[s];
+      oi[pos] = static_cast<IdxT>(col(s));
+    }
+    base += popc(msk);
+  }
+}
+
+// Order-key bisection until a count equals k or lo, hi are adjacent floats
+// (at most 32 counts), then the emission.
+template <int S, typename IdxT, typename ColFn>
+__device__ __forceinline__ void finish_by_keys(const float (&v)[S], ColFn col,
+                                               int k, float lo, float hi,
+                                               float* __restrict__ ov,
+                                               IdxT* __restrict__ oi) {
+  int32_t klo = order_key(lo);
+  int32_t khi = order_key(hi);
+#pragma unroll 1
+  for (;;) {
+    const uint32_t width = static_cast<uint32_t>(khi) - static_cast<uint32_t>(klo);
+    if (width <= 1u) break;
+    const int32_t kmid =
+        static_cast<int32_t>(static_cast<uint32_t>(klo) + (width >> 1));
+    const float t = key_value(kmid);
+    const int c = count_ge(v, t);
+    if (c == k) {
+      emit_ge(v, col, t, ov, oi);
+      return;
+    }
+    const bool up = c > k;
+    klo = up ? kmid : klo;
+    khi = up ? khi : kmid;
+  }
+  emit_fill(v, col, key_value(klo), key_value(khi), k, ov, oi);
+}
+
+// The candidates left after compaction: QC slots in column order (unused
+// lanes hold -inf). Newton steps toward k + 1/2 elements from the count c at
+// lo; then snaps, each of which settles one distinct value: from above,
+// u = largest candidate below hi is the k-th largest iff #{x >= u} >= k;
+// from below, u = smallest candidate >= lo is iff #{x > u} <= k. The side
+// with fewer values to settle is taken.
+template <int QC, typename IdxT>
+__device__ __forceinline__ void exact_candidates(const float (&cv)[QC],
+                                                 const int (&ci)[QC], int k,
+                                                 float lo, int clo, float h,
+                                                 float* __restrict__ ov,
+                                                 IdxT* __restrict__ oi) {
+  auto col = [&ci](int s) { return ci[s]; };
+  float hi = kInf;
+  int chi = 0;
+  float t = lo;
+  int c = clo;
+  const int target2 = 2 * k + 1;
+#pragma unroll 1
+  for (int it = 0;;) {
+    t = fmaf(static_cast<float>(2 * c - target2), h, t);
+    c = count_ge(cv, t);
+    if (c == k || ++it == kCandSteps) break;
+    const bool up = c > k;
+    lo = up ? t : lo;
+    clo = up ? c : clo;
+    hi = up ? hi : t;
+    chi = up ? chi : c;
+  }
+  if (c == k) {
+    emit_ge(cv, col, t, ov, oi);
+    return;
+  }
+  {
+    const bool up = c > k;
+    lo = up ? t : lo;
+    clo = up ? c : clo;
+    hi = up ? hi : t;
+    chi = up ? chi : c;
+  }
+#pragma unroll 1
+  for (int it = 0; it < kCandSnaps; ++it) {
+    const int need = k - chi;           // survivors still to take from [lo, hi)
+    const int span = clo - chi;         // candidates in [lo, hi)
+    if (need <= span - need + 1) {
+      float u = -kInf;
+#pragma unroll
+      for (int s = 0; s < QC; ++s) u = fmaxf(u, cv[s] < hi ? cv[s] : -kInf);
+      u = wave_max(u);
+      const int cu = count_ge(cv, u);
+      if (cu >= k) {
+        emit_fill(cv, col, u, hi, k, ov, oi);
+        return;
+      }
+      hi = u;
+      chi = cu;
+    } else {
+      float u = kInf;
+#pragma unroll
+      for (int s = 0; s < QC; ++s) u = fminf(u, cv[s] >= lo ? cv[s] : kInf);
+      u = wave_min(u);
+      const float above = next_float(u);
+      const int cg = count_ge(cv, above);
+      if (cg <= k) {
+        emit_fill(cv, col, u, above, k, ov, oi);
+        return;
+      }
+      lo = above;
+      clo = cg;
+    }
+  }
+  finish_by_keys(cv, col, k, lo, hi, ov, oi);
+}
+
+template <int Q, bool FULL, int QC, typename IdxT>
+__device__ __forceinline__ void exact_row(const float (&vin)[Q],
+                                          const SelectArgs& a, int lane,
+                                          uint2* __restrict__ scratch,
+                                          float* __restrict__ ov,
+                                          IdxT* __restrict__ oi) {
+  const int k = a.k;
+  float v[Q];
+  // Root mean square of the row: the scale of the model behind the
+  // thresholds (the model assumes rows centred near zero; the Newton steps
+  // below correct the first threshold when they are not).
+  float s2 = 0.0f;
+#pragma unroll
+  for (int s = 0; s < Q; ++s) {
+    const float x = in_row<FULL>(s, a.m, lane) ? vin[s] : 0.0f;
+    v[s] = vin[s];
+    s2 = fmaf(x, x, s2);
+  }
+  s2 = wave_sum(s2);
+  // Squares of values beyond ~1.8e19 overflow: give up on the model then
+  // (thresholds stay finite and the order-key bisection does the work).
+  s2 = s2 < kInf ? s2 : 0.0f;
+  mask_tail<Q, FULL>(a.m, lane, v);
+  // Raw hardware square root: the model only steers the search.
+  const float rms = __builtin_amdgcn_sqrtf(s2 * a.inv_m);
+  const float h = rms * a.half_step_per_sd;
+  float t = rms * a.z_first;
+  float lo = -kInf, hi = kInf;
+  // Counts aimed at: the middle of (k, W] while looking for candidates,
+  // k + 1/2 otherwise (doubled to stay integral).
+  constexpr int kW = kWave * QC;
+  const int target2 = QC > 0 ? k + kW : 2 * k + 1;
+  auto col = [lane](int s) { return s * kWave + lane; };
+  int c;
+#pragma unroll 1
+  for (int it = 0;;) {
+    c = count_ge(v, t);
+    if (c == k || (QC > 0 && c > k && c <= kW) || ++it == kRowSteps) break;
+    const bool up = c > k;
+    lo = up ? t : lo;
+    hi = up ? hi : t;
+    t = fmaf(static_cast<float>(2 * c - target2), h, t);
+  }
+  if (c == k) {
+    emit_ge(v, col, t, ov, oi);
+    return;
+  }
+  if constexpr (QC > 0) {
+    if (c > k && c <= kW) {
+      // Compact {x >= t} (every element the result can hold) into LDS in
+      // column order as (value bits, column) pairs; read back QC slots.
+      uint32_t base = 0;
+#pragma unroll
+      for (int s = 0; s < Q; ++s) {
+        const uint64_t msk = ballot(v[s] >= t);
+        if (__builtin_amdgcn_inverse_ballot_w64(msk)) {
+          scratch[rank_below(msk, base)] =
+              make_uint2(__float_as_uint(v[s]), static_cast<uint32_t>(col(s)));
+        }
+        base += popc(msk);
+      }
+      // LDS operations of one wave complete in issue order; the barrier
+      // only keeps the compiler from moving the reads above the writes.
+      __builtin_amdgcn_wave_barrier();
+      float cv[QC];
+      int ci[QC];
+#pragma unroll
+      for (int j = 0; j < QC; ++j) {
+        const int e = j * kWave + lane;
+        const uint2 w = scratch[e];
+        cv[j] = e < c ? __uint_as_float(w.x) : -kInf;
+        ci[j] = static_cast<int>(w.y);
+      }
+      __builtin_amdgcn_wave_barrier();
+      exact_candidates<QC>(cv, ci, k, t, c, h, ov, oi);
+      return;
+    }
+  }
+  const bool up = c > k;
+  lo = up ? t : lo;
+  hi = up ? hi : t;
+  finish_by_keys(v, col, k, lo, hi, ov, oi);
+}
+
+// ---------------------------------------------------------------------------
+// The kernel: persistent waves, one row at a time, next rows prefetched.
+// ---------------------------------------------------------------------------
+template <int Q, bool FULL, Mode MODE, int QC, typename IdxT>
+__device__ __forceinline__ void process_row(const float (&v)[Q],
+                                            const SelectArgs& a, int lane,
+                                            uint2* __restrict__ scratch,
+                                            float* __restrict__ ov,
+                                            IdxT* __restrict__ oi) {
+  if constexpr (MODE == Mode::kExact)
+    exact_row<Q, FULL, QC, IdxT>(v, a, lane, scratch, ov, oi);
+  else
+    capped_row<Q, FULL, IdxT>(v, a, lane, ov, oi);
+}
+
+// Rows each wave keeps in flight: the row being worked on plus D - 1
+// prefetched ones. The prefetch loads are unconditional (past the last row
+// they re-read it) so that the compiler's wait counts stay exact and a
+// wave only ever waits for the row it is about to use.
+template <int Q>
+constexpr int prefetch_depth() {
+  return Q <= 4 ? 3 : (Q <= 16 ? 2 : 1);
+}
+
+template <int Q, bool FULL, Mode MODE, int QC, typename IdxT>
+__global__ __launch_bounds__(kBlock) void rows_in_registers(SelectArgs a) {
+  // Per wave: room for 64*QC compacted (value, column) candidates.
+  constexpr int kScratch = (MODE == Mode::kExact && QC > 0) ? kWave * QC : 1;
+  constexpr int D = prefetch_depth<Q>();
+  __shared__ uint2 scratch_all[kWavesPerBlock][kScratch];
+  const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+  const int wave_in_block =
+      __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  uint2* scratch = scratch_all[wave_in_block];
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+  int64_t r = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_in_block;
+  if (r >= a.n) return;
+  // Row pointers advance by constant steps (no per-row 64-bit multiply).
+  const int64_t m = a.m, k = a.k;
+  const float* const x_last = a.x + (a.n - 1) * m;
+  const int64_t x_step = stride * m;
+  const float* xp = a.x + r * m;           // row r
+  float* ov = a.out_val + r * k;
+  IdxT* oi = static_cast<IdxT*>(a.out_idx) + r * k;
+  const int64_t o_step = stride * k;
+  float buf[D][Q];
+#pragma unroll
+  for (int d = 0; d + 1 < D; ++d) {
+    const float* p = xp + d * x_step;
+    load_row<Q, FULL>(p < x_last ? p : x_last, a.m, lane, buf[d]);
+  }
+  for (;;) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      // buf[d] holds row r; refill the buffer freed by the previous row.
+      const float* p = xp + (D - 1) * x_step;
+      load_row<Q, FULL>(p < x_last ? p : x_last, a.m, lane, buf[(d + D - 1) % D]);
+      process_row<Q, FULL, MODE, QC, IdxT>(buf[d], a, lane, scratch, ov, oi);
+      r += stride;
+      if (r >= a.n) return;
+      xp += x_step;
+      ov += o_step;
+      oi += o_step;
+    }
+  }
+}
+
+// Candidate slot counts QC the exact kernels are built with for Q slots:
+// 0 (no compaction) and the powers of two up to Q/2.
+constexpr bool exact_qc_built(int q, int qc) {
+  return qc == 0 || ((qc == 1 || qc == 2 || qc == 4 || qc == 8) && 2 * qc <= q);
+}
+
+template <int Q, bool FULL, typename IdxT>
+RowsKernel exact_kernel(int qc) {
+  switch (qc) {
+    case 1:
+      if constexpr (exact_qc_built(Q, 1))
+        return rows_in_registers<Q, FULL, Mode::kExact, 1, IdxT>;
+      break;
+    case 2:
+      if constexpr (exact_qc_built(Q, 2))
+        return rows_in_registers<Q, FULL, Mode::kExact, 2, IdxT>;
+      break;
+    case 4:
+      if constexpr (exact_qc_built(Q, 4))
+        return rows_in_registers<Q, FULL, Mode::kExact, 4, IdxT>;
+      break;
+    case 8:
+      if constexpr (exact_qc_built(Q, 8))
+        return rows_in_registers<Q, FULL, Mode::kExact, 8, IdxT>;
+      break;
+    default:
+      break;
+  }
+  return rows_in_registers<Q, FULL, Mode::kExact, 0, IdxT>;
+}
+
+template <int Q, bool FULL, typename IdxT>
+RowsKernel any_kernel(Mode mode, int qc) {
+  if (mode == Mode::kExact) return exact_kernel<Q, FULL, IdxT>(qc);
+  return rows_in_registers<Q, FULL, Mode::kCapped, 0, IdxT>;
+}
+
+}  // namespace rows_detail
+
+// The row kernel for Q slots per lane (row length up to 64*Q), one of the
+// buckets listed in rtopk_internal.h. full: the row length is exactly 64*Q
+// (only distinguished for Q <= 4). qc: candidate slots for the exact search
+// (see candidate_slots). Returns nullptr for one-byte indices with Q > 4.
+template <int Q>
+RowsKernel rows_kernel(bool full, Mode mode, bool u8_index, int qc) {
+  using rows_detail::any_kernel;
+  if (u8_index) {
+    if constexpr (Q <= 4) {
+      return full ? any_kernel<Q, true, uint8_t>(mode, qc)
+                  : any_kernel<Q, false, uint8_t>(mode, qc);
+    } else {
+      return nullptr;
+    }
+  }
+  if constexpr (Q <= 4) {
+    if (full) return any_kernel<Q, true, int32_t>(mode, qc);
+  }
+  return any_kernel<Q, false, int32_t>(mode, qc);
+}
+
+}  // namespace rtopk

@@ -1,0 +1,99 @@
+"""The C ABI (include/rtopk.h): symbols, status strings and host-side
+validation. Runs without a GPU: every call here is rejected (or is the N = 0
+no-op) before the library touches the HIP runtime."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import row_wise_top_amd as rt
+from row_wise_top_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "rtopk.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rtopk_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted([
+        "rtopk_select", "rtopk_select_exact", "rtopk_select_u8",
+        "rtopk_select_exact_u8", "rtopk_status_string"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(4):
+        s = rt.rtopk_status_string(code)
+        assert isinstance(s, str) and s
+    assert rt.rtopk_status_string(0) == "success"
+    assert rt.rtopk_status_string(99) == "unknown status"
+
+
+def call(fn, *args):
+    return getattr(rt.lib(), fn)(*args)
+
+
+CAPPED = ["rtopk_select", "rtopk_select_u8"]
+EXACT = ["rtopk_select_exact", "rtopk_select_exact_u8"]
+FAKE = 0x1000  # never dereferenced: every case below fails validation first
+
+
+@pytest.mark.parametrize("fn", CAPPED + EXACT)
+def test_n_zero_is_a_noop(fn):
+    if fn in CAPPED:
+        assert call(fn, None, 0, 16, 4, -1, 0.0, None, None, None) == 0
+    else:
+        assert call(fn, None, 0, 16, 4, None, None, None) == 0
+
+
+@pytest.mark.parametrize("fn", CAPPED + EXACT)
+@pytest.mark.parametrize("n,m,k,code", [
+    (-1, 16, 4, 1),      # N < 0
+    (4, 0, 1, 1),        # M < 1
+    (4, 16, 0, 1),       # k < 1
+    (4, 16, 17, 1),      # k > M
+    (4, 8193, 4, 2),     # M above the supported maximum
+])
+def test_shape_errors(fn, n, m, k, code):
+    if fn in CAPPED:
+        rc = call(fn, FAKE, n, m, k, -1, 0.0, FAKE, FAKE, None)
+    else:
+        rc = call(fn, FAKE, n, m, k, FAKE, FAKE, None)
+    assert rc == code
+
+
+@pytest.mark.parametrize("fn", ["rtopk_select_u8", "rtopk_select_exact_u8"])
+def test_u8_requires_short_rows(fn):
+    if fn in CAPPED:
+        assert call(fn, FAKE, 4, 257, 4, -1, 0.0, FAKE, FAKE, None) == 2
+    else:
+        assert call(fn, FAKE, 4, 257, 4, FAKE, FAKE, None) == 2
+
+
+@pytest.mark.parametrize("fn", CAPPED)
+@pytest.mark.parametrize("eps", [-1.0, float("nan"), -1e-30])
+def test_bad_eps(fn, eps):
+    assert call(fn, FAKE, 4, 16, 4, -1, eps, FAKE, FAKE, None) == 1
+
+
+@pytest.mark.parametrize("fn", CAPPED + EXACT)
+@pytest.mark.parametrize("which", [0, 1, 2])
+def test_null_pointers(fn, which):
+    ptrs = [FAKE, FAKE, FAKE]
+    ptrs[which] = None
+    if fn in CAPPED:
+        rc = call(fn, ptrs[0], 4, 16, 4, -1, 0.0, ptrs[1], ptrs[2], None)
+    else:
+        rc = call(fn, ptrs[0], 4, 16, 4, ptrs[1], ptrs[2], None)
+    assert rc == 1

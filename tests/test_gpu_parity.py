@@ -1,0 +1,248 @@
+"""GPU parity: the HIP kernels against the CPU oracle, bit for bit.
+
+Selection does no arithmetic on the values it returns, so the bar is exact
+identity: the same column indices and the same value bits as the oracle, for
+the exact mode (lowest index wins ties on both sides) and for the capped
+search with the same max_iter / eps. Inputs come from workloads.py (seeded);
+every expected value comes from oracle/.
+
+Workloads: the five named shapes (full size where the oracle finishes in
+seconds; sampled rows for the 4 GiB one), adversarial rows at many row
+lengths (ties, +-0, subnormals, +-FLT_MAX, constant rows), ragged row counts,
+and guard bands around the outputs.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def rt():
+    import row_wise_top_amd
+    return row_wise_top_amd
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def gpu_run(x_np, k, mode, max_iter=-1, eps=0.0, u8=False):
+    x = torch.from_numpy(np.ascontiguousarray(x_np)).to(dev())
+    return gpu_run_t(x, k, mode, max_iter, eps, u8)
+
+
+def gpu_run_t(x, k, mode, max_iter=-1, eps=0.0, u8=False):
+    r = rt()
+    if mode == "exact":
+        v, i = (r.rtopk_select_exact_u8 if u8 else r.rtopk_select_exact)(x, k)
+    else:
+        v, i = (r.rtopk_select_u8 if u8 else r.rtopk_select)(x, k, max_iter, eps)
+    torch.cuda.synchronize()
+    return v.cpu().numpy(), i.cpu().numpy().astype(np.int32)
+
+
+def oracle_run(x_np, k, mode, max_iter=-1, eps=0.0):
+    if mode == "exact":
+        return oracle.exact(x_np, k)
+    return oracle.capped(x_np, k, max_iter, eps)
+
+
+def assert_identical(got, want, label):
+    gv, gi = got
+    wv, wi = want
+    bad_rows = np.flatnonzero((gi != wi).any(axis=1) |
+                              (gv.view(np.uint32) != wv.view(np.uint32)).any(axis=1))
+    assert bad_rows.size == 0, (
+        f"{label}: {bad_rows.size} rows differ, first {bad_rows[:5].tolist()}; "
+        f"row {bad_rows[0]}: got idx {gi[bad_rows[0]][:16].tolist()} "
+        f"want {wi[bad_rows[0]][:16].tolist()}")
+
+
+def check(x_np, k, mode, max_iter=-1, eps=0.0, u8=False, label=""):
+    print(f"[parity] {label} N={x_np.shape[0]} M={x_np.shape[1]} k={k} {mode} "
+          f"max_iter={max_iter} eps={eps} u8={u8}", flush=True)
+    got = gpu_run(x_np, k, mode, max_iter, eps, u8)
+    want = oracle_run(x_np, k, mode, max_iter, eps)
+    assert_identical(got, want, label)
+
+
+# ---------------------------------------------------------------------------
+# Named workloads
+# ---------------------------------------------------------------------------
+
+def test_workload1_exact_and_uncapped():
+    x = workloads.config_input(1)
+    for u8 in (False, True):
+        check(x, 32, "exact", u8=u8, label="w1")
+        check(x, 32, "capped", -1, 0.0, u8=u8, label="w1-uncapped")
+
+
+@pytest.fixture(scope="module")
+def w2():
+    return workloads.config_input(2)
+
+
+@pytest.mark.parametrize("k", [16, 32, 64, 128])
+def test_workload2_sweep(w2, k):
+    x = torch.from_numpy(w2).to(dev())
+    print(f"[parity] w2 k={k} exact", flush=True)
+    assert_identical(gpu_run_t(x, k, "exact"), oracle.exact(w2, k), f"w2 exact k={k}")
+    for eps in (0.0, 1e-4):
+        for max_iter in (-1, 2, 3, 4, 5):
+            print(f"[parity] w2 k={k} eps={eps} max_iter={max_iter}", flush=True)
+            got = gpu_run_t(x, k, "capped", max_iter, eps)
+            want = oracle.capped(w2, k, max_iter, eps)
+            assert_identical(got, want, f"w2 k={k} eps={eps} max_iter={max_iter}")
+
+
+def test_workload3_full_size():
+    x = workloads.config_input(3)
+    print("[parity] w3 full 262144x256 exact u8", flush=True)
+    xt = torch.from_numpy(x).to(dev())
+    want = oracle.exact(x, 32)
+    assert_identical(gpu_run_t(xt, 32, "exact", u8=True), want, "w3 exact u8")
+    assert_identical(gpu_run_t(xt, 32, "exact", u8=False), want, "w3 exact i32")
+    assert_identical(gpu_run_t(xt, 32, "capped", -1, 0.0, u8=True), want, "w3 uncapped u8")
+
+
+@pytest.mark.parametrize("m", [512, 1024, 2048, 4096, 8192])
+def test_workload4_ties(m):
+    x = workloads.config_input(4, m=m)
+    xt = torch.from_numpy(x).to(dev())
+    for k in (32, 64, 128, 256):
+        print(f"[parity] w4 M={m} k={k} exact", flush=True)
+        assert_identical(gpu_run_t(xt, k, "exact"), oracle.exact(x, k), f"w4 M={m} k={k}")
+    print(f"[parity] w4 M={m} k=256 uncapped", flush=True)
+    assert_identical(gpu_run_t(xt, 256, "capped", -1, 0.0), oracle.exact(x, 256),
+                     f"w4 M={m} uncapped")
+
+
+def test_workload5_sampled_rows():
+    """1,048,576 x 1,024 (4 GiB): all rows on the GPU, sampled rows checked,
+    including the last rows (byte offsets beyond 2^32)."""
+    x = workloads.config_input(5)
+    n = x.shape[0]
+    rng = np.random.default_rng(123)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(n - 64, n),
+                                     rng.integers(0, n, size=4000)]))
+    xs = np.ascontiguousarray(x[rows])
+    xt = torch.from_numpy(x).to(dev())
+    del x
+    for mi in (2, 3, 4, 5, 6, 7, 8):
+        print(f"[parity] w5 max_iter={mi}", flush=True)
+        v, i = gpu_run_t(xt, 64, "capped", mi, 0.0)
+        assert_identical((v[rows], i[rows]), oracle.capped(xs, 64, mi, 0.0), f"w5 max_iter={mi}")
+    print("[parity] w5 exact", flush=True)
+    v, i = gpu_run_t(xt, 64, "exact")
+    assert_identical((v[rows], i[rows]), oracle.exact(xs, 64), "w5 exact")
+    del xt
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# Edge cases
+# ---------------------------------------------------------------------------
+
+ROW_LENGTHS = [1, 2, 5, 31, 63, 64, 65, 100, 127, 128, 129, 191, 192, 200, 255,
+               256, 257, 300, 383, 384, 500, 512, 700, 1000, 1024, 1500, 2047,
+               2048, 3000, 4095, 4096, 6000, 8191, 8192]
+
+
+@pytest.mark.parametrize("m", ROW_LENGTHS)
+def test_adversarial_rows(m):
+    x = workloads.adversarial_rows(m)
+    ks = sorted({k for k in (1, 2, m // 3, m - 1, m) if 1 <= k <= m})
+    for k in ks:
+        check(x, k, "exact", label=f"adv M={m}")
+        if m <= 256:
+            check(x, k, "exact", u8=True, label=f"adv M={m}")
+        for mi, eps in ((-1, 0.0), (0, 0.0), (1, 0.0), (3, 0.0), (-1, 0.5), (6, 1e-3)):
+            check(x, k, "capped", mi, eps, label=f"adv M={m}")
+            if m <= 256 and mi in (-1, 3):
+                check(x, k, "capped", mi, eps, u8=True, label=f"adv M={m}")
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 7, 1023, 4097, 30001])
+def test_ragged_row_counts(n):
+    m = 256 if n < 30000 else 100
+    x = workloads.normal(n, m, seed=n)
+    check(x, 7, "exact", label="ragged")
+    check(x, 7, "capped", 4, 0.0, label="ragged")
+
+
+def test_random_shapes_ties_and_scales():
+    rng = np.random.default_rng(2024)
+    for t in range(40):
+        m = int(rng.integers(1, 1400))
+        n = int(rng.integers(1, 300))
+        k = int(rng.integers(1, m + 1))
+        kind = t % 4
+        if kind == 0:
+            x = rng.standard_normal((n, m)).astype(np.float32)
+        elif kind == 1:
+            x = rng.integers(-3, 4, size=(n, m)).astype(np.float32)
+        elif kind == 2:
+            x = (rng.standard_normal((n, m)) * 10.0 ** rng.integers(-40, 37)).astype(np.float32)
+        else:
+            x = (rng.integers(-5, 6, size=(n, m)) * np.finfo(np.float32).smallest_subnormal).astype(np.float32)
+        check(x, k, "exact", label=f"rand{t}")
+        check(x, k, "capped", int(rng.integers(-1, 12)), float(rng.choice([0.0, 1e-3, 0.25])),
+              label=f"rand{t}")
+
+
+def test_outputs_untouched_outside_bounds_and_deterministic():
+    n, m, k = 777, 300, 40
+    x = torch.from_numpy(workloads.normal(n, m, seed=5)).to(dev())
+    guard = 4096
+    vbuf = torch.full((n * k + 2 * guard,), 12345.0, dtype=torch.float32, device=dev())
+    ibuf = torch.full((n * k + 2 * guard,), -777, dtype=torch.int32, device=dev())
+    ov = vbuf[guard:guard + n * k].view(n, k)
+    oi = ibuf[guard:guard + n * k].view(n, k)
+    r = rt()
+    r.rtopk_select_exact(x, k, out_val=ov, out_idx=oi)
+    torch.cuda.synchronize()
+    first = (ov.cpu().numpy().copy(), oi.cpu().numpy().copy())
+    assert (vbuf[:guard] == 12345.0).all() and (vbuf[-guard:] == 12345.0).all()
+    assert (ibuf[:guard] == -777).all() and (ibuf[-guard:] == -777).all()
+    for _ in range(3):
+        r.rtopk_select_exact(x, k, out_val=ov, out_idx=oi)
+        torch.cuda.synchronize()
+        assert (ov.cpu().numpy() == first[0]).all() and (oi.cpu().numpy() == first[1]).all()
+
+
+def test_python_binding_errors_on_gpu():
+    r = rt()
+    x = torch.zeros((4, 300), dtype=torch.float32, device=dev())
+    with pytest.raises(ValueError):
+        r.rtopk_select(x, 0)
+    with pytest.raises(ValueError):
+        r.rtopk_select(x, 301)
+    with pytest.raises(ValueError):
+        r.rtopk_select(x, 3, eps=-1.0)
+    with pytest.raises(NotImplementedError):
+        r.rtopk_select_u8(x, 3)
+    with pytest.raises(NotImplementedError):
+        r.rtopk_select_exact(torch.zeros((2, 8193), device=dev()), 3)
+    with pytest.raises(ValueError):
+        r.rtopk_select(x.double(), 3)
+    with pytest.raises(ValueError):
+        r.rtopk_select(x.t(), 3)
+    v, i = r.rtopk_select_exact(torch.zeros((0, 16), device=dev()), 3)
+    assert v.shape == (0, 3) and i.shape == (0, 3)
+
+
+def test_nonnull_stream():
+    r = rt()
+    x_np = workloads.normal(3000, 256, seed=9)
+    x = torch.from_numpy(x_np).to(dev())
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        v, i = r.rtopk_select_exact(x, 32)
+    s.synchronize()
+    assert_identical((v.cpu().numpy(), i.cpu().numpy()), oracle.exact(x_np, 32), "stream")
