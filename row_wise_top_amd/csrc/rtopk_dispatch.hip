@@ -126,7 +126,7 @@ hipError_t launch_select(const SelectArgs& args, Mode mode, bool u8_index,
   hipError_t err = hipGetDevice(&device);
   if (err != hipSuccess) return err;
   // One wave per row at a time; a persistent grid of what fits on the device
-  // at once, each wave striding over the rows.
+  // at once (each wave takes rows in groups, so fewer waves may suffice).
   const int64_t blocks_needed = (a.n + kWavesPerBlock - 1) / kWavesPerBlock;
   const int64_t resident =
       static_cast<int64_t>(cu_count(device)) *

@@ -576,6 +576,10 @@ constexpr int prefetch_depth() {
   return Q <= 4 ? 3 : (Q <= 16 ? 2 : 1);
 }
 
+// Row order. Wave w of S works through groups of D consecutive rows:
+// group g is rows (g*S + w)*D ... (g*S + w)*D + D - 1. The rows a wave has in
+// flight are neighbours, and at any moment all waves together read one
+// contiguous stretch of the matrix (HBM streams fastest that way).
 template <int Q, bool FULL, Mode MODE, int QC, typename IdxT>
 __global__ __launch_bounds__(kBlock) void rows_in_registers(SelectArgs a) {
   // Per wave: room for 64*QC compacted (value, column) candidates.
@@ -586,36 +590,39 @@ __global__ __launch_bounds__(kBlock) void rows_in_registers(SelectArgs a) {
   const int wave_in_block =
       __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   uint2* scratch = scratch_all[wave_in_block];
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
-  int64_t r = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_in_block;
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_in_block;
+  int64_t r = w * D;  // first row of the current group
   if (r >= a.n) return;
-  // Row pointers advance by constant steps (no per-row 64-bit multiply).
+  // Pointers advance by constant steps (no per-row 64-bit multiply).
   const int64_t m = a.m, k = a.k;
   const float* const x_last = a.x + (a.n - 1) * m;
-  const int64_t x_step = stride * m;
-  const float* xp = a.x + r * m;           // row r
-  float* ov = a.out_val + r * k;
-  IdxT* oi = static_cast<IdxT*>(a.out_idx) + r * k;
-  const int64_t o_step = stride * k;
+  const int64_t group_rows = waves * D;
+  const float* xg = a.x + r * m;  // current group
+  float* og = a.out_val + r * k;
+  IdxT* ig = static_cast<IdxT*>(a.out_idx) + r * k;
   float buf[D][Q];
 #pragma unroll
   for (int d = 0; d + 1 < D; ++d) {
-    const float* p = xp + d * x_step;
+    const float* p = xg + d * m;
     load_row<Q, FULL>(p < x_last ? p : x_last, a.m, lane, buf[d]);
   }
   for (;;) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      // buf[d] holds row r; refill the buffer freed by the previous row.
-      const float* p = xp + (D - 1) * x_step;
+      // buf[d] holds row r + d. Refill the buffer freed by the previous row
+      // with the row D - 1 places further on in this wave's order.
+      const float* p = d == 0 ? xg + (D - 1) * m : xg + (group_rows + d - 1) * m;
       load_row<Q, FULL>(p < x_last ? p : x_last, a.m, lane, buf[(d + D - 1) % D]);
-      process_row<Q, FULL, MODE, QC, IdxT>(buf[d], a, lane, scratch, ov, oi);
-      r += stride;
-      if (r >= a.n) return;
-      xp += x_step;
-      ov += o_step;
-      oi += o_step;
+      if (r + d >= a.n) return;
+      process_row<Q, FULL, MODE, QC, IdxT>(buf[d], a, lane, scratch, og + d * k,
+                                           ig + d * k);
     }
+    r += group_rows;
+    if (r >= a.n) return;
+    xg += group_rows * m;
+    og += group_rows * k;
+    ig += group_rows * k;
   }
 }
 
