@@ -318,7 +318,7 @@ __device__ __forceinline__ void capped_row(const float (&vin)[Q],
 // Full-row Newton steps before the order-key bisection takes over.
 constexpr int kRowSteps = 4;
 // Newton steps, then snaps, on the compacted candidates.
-constexpr int kCandSteps = 6;
+constexpr int kCandSteps = 5;
 constexpr int kCandSnaps = 4;
 
 __device__ __forceinline__ float wave_min(float a) {
@@ -394,46 +394,17 @@ __device__ __forceinline__ void finish_by_keys(const float (&v)[S], ColFn col,
   emit_fill(v, col, key_value(klo), key_value(khi), k, ov, oi);
 }
 
-// The candidates left after compaction: QC slots in column order (unused
-// lanes hold -inf). Newton steps toward k + 1/2 elements from the count c at
-// lo; then snaps, each of which settles one distinct value: from above,
+// Snaps, then order-key bisection, on the candidates once the Newton steps
+// have not hit k exactly. Each snap settles one distinct value: from above,
 // u = largest candidate below hi is the k-th largest iff #{x >= u} >= k;
 // from below, u = smallest candidate >= lo is iff #{x > u} <= k. The side
 // with fewer values to settle is taken.
-template <int QC, typename IdxT>
-__device__ __forceinline__ void exact_candidates(const float (&cv)[QC],
-                                                 const int (&ci)[QC], int k,
-                                                 float lo, int clo, float h,
-                                                 float* __restrict__ ov,
-                                                 IdxT* __restrict__ oi) {
-  auto col = [&ci](int s) { return ci[s]; };
-  float hi = kInf;
-  int chi = 0;
-  float t = lo;
-  int c = clo;
-  const int target2 = 2 * k + 1;
-#pragma unroll 1
-  for (int it = 0;;) {
-    t = fmaf(static_cast<float>(2 * c - target2), h, t);
-    c = count_ge(cv, t);
-    if (c == k || ++it == kCandSteps) break;
-    const bool up = c > k;
-    lo = up ? t : lo;
-    clo = up ? c : clo;
-    hi = up ? hi : t;
-    chi = up ? chi : c;
-  }
-  if (c == k) {
-    emit_ge(cv, col, t, ov, oi);
-    return;
-  }
-  {
-    const bool up = c > k;
-    lo = up ? t : lo;
-    clo = up ? c : clo;
-    hi = up ? hi : t;
-    chi = up ? chi : c;
-  }
+template <int QC, typename IdxT, typename ColFn>
+__device__ __forceinline__ void settle_candidates(const float (&cv)[QC],
+                                                  ColFn col, int k, float lo,
+                                                  int clo, float hi, int chi,
+                                                  float* __restrict__ ov,
+                                                  IdxT* __restrict__ oi) {
 #pragma unroll 1
   for (int it = 0; it < kCandSnaps; ++it) {
     const int need = k - chi;           // survivors still to take from [lo, hi)
@@ -468,6 +439,140 @@ __device__ __forceinline__ void exact_candidates(const float (&cv)[QC],
   finish_by_keys(cv, col, k, lo, hi, ov, oi);
 }
 
+// The candidates left after compaction: QC slots in column order (unused
+// lanes hold -inf), all elements >= t0, with c0 = #{x >= t0} in (k, 64*QC].
+// A fixed number of Newton steps toward k + 1/2 elements runs straight
+// through (no bracket bookkeeping); a count of exactly k ends it. Otherwise
+// the bracket is rebuilt from the recorded steps and the row is settled.
+template <int QC, typename IdxT>
+__device__ __forceinline__ void exact_candidates(const float (&cv)[QC],
+                                                 const int (&ci)[QC], int k,
+                                                 float t0, int c0, float h,
+                                                 float* __restrict__ ov,
+                                                 IdxT* __restrict__ oi) {
+  auto col = [&ci](int s) { return ci[s]; };
+  const int target2 = 2 * k + 1;
+  float ts[kCandSteps];
+  int cs[kCandSteps];
+  float t = t0;
+  int c = c0;
+  int steps = 0;
+#pragma unroll
+  for (int i = 0; i < kCandSteps; ++i) {
+    t = fmaf(static_cast<float>(2 * c - target2), h, t);
+    c = count_ge(cv, t);
+    ts[i] = t;
+    cs[i] = c;
+    steps = i + 1;
+    if (c == k) break;
+  }
+  if (c == k) {
+    emit_ge(cv, col, t, ov, oi);
+    return;
+  }
+  // Tightest bracket seen: every count gave a valid bound.
+  float lo = t0, hi = kInf;
+  int clo = c0, chi = 0;
+#pragma unroll
+  for (int i = 0; i < kCandSteps; ++i) {
+    if (i < steps) {
+      if (cs[i] > k && ts[i] > lo) {
+        lo = ts[i];
+        clo = cs[i];
+      }
+      if (cs[i] < k && ts[i] < hi) {
+        hi = ts[i];
+        chi = cs[i];
+      }
+    }
+  }
+  settle_candidates<QC>(cv, col, k, lo, clo, hi, chi, ov, oi);
+}
+
+// Full-row search when the first count missed the candidate window: Newton
+// steps on the whole row (compacting as soon as a count lands in (k, W]),
+// then order-key bisection.
+template <int Q, int QC, typename IdxT>
+__device__ __noinline__ void exact_row_search(const float (&v)[Q], int k,
+                                              int lane, float t, int c,
+                                              float h,
+                                              uint2* __restrict__ scratch,
+                                              float* __restrict__ ov,
+                                              IdxT* __restrict__ oi);
+
+template <int Q, int QC, typename IdxT>
+__device__ __forceinline__ void compact_and_search(const float (&v)[Q], int k,
+                                                   int lane, float t, int c,
+                                                   float h,
+                                                   uint2* __restrict__ scratch,
+                                                   float* __restrict__ ov,
+                                                   IdxT* __restrict__ oi) {
+  // Compact {x >= t} (every element the result can hold) into LDS in
+  // column order as (value bits, column) pairs. Lanes whose element is not
+  // a candidate write a per-lane spare entry instead, so the writes need no
+  // exec-mask switching.
+  constexpr int kW = kWave * QC;
+  uint32_t base = 0;
+#pragma unroll
+  for (int s = 0; s < Q; ++s) {
+    const uint64_t msk = ballot(v[s] >= t);
+    const uint32_t pos = rank_below(msk, base);
+    const uint32_t e = __builtin_amdgcn_inverse_ballot_w64(msk)
+                           ? pos
+                           : static_cast<uint32_t>(kW + lane);
+    scratch[e] = make_uint2(__float_as_uint(v[s]),
+                            static_cast<uint32_t>(s * kWave + lane));
+    base += popc(msk);
+  }
+  // LDS operations of one wave complete in issue order; the barrier only
+  // keeps the compiler from moving the reads above the writes.
+  __builtin_amdgcn_wave_barrier();
+  float cv[QC];
+  int ci[QC];
+#pragma unroll
+  for (int j = 0; j < QC; ++j) {
+    const int e = j * kWave + lane;
+    const uint2 w = scratch[e];
+    cv[j] = e < c ? __uint_as_float(w.x) : -kInf;
+    ci[j] = static_cast<int>(w.y);
+  }
+  __builtin_amdgcn_wave_barrier();
+  exact_candidates<QC>(cv, ci, k, t, c, h, ov, oi);
+}
+
+template <int Q, int QC, typename IdxT>
+__device__ __noinline__ void exact_row_search(const float (&v)[Q], int k,
+                                              int lane, float t, int c,
+                                              float h,
+                                              uint2* __restrict__ scratch,
+                                              float* __restrict__ ov,
+                                              IdxT* __restrict__ oi) {
+  constexpr int kW = kWave * QC;
+  const int target2 = QC > 0 ? k + kW : 2 * k + 1;
+  auto col = [lane](int s) { return s * kWave + lane; };
+  float lo = -kInf, hi = kInf;
+#pragma unroll 1
+  for (int it = 1;; ++it) {
+    const bool up = c > k;
+    lo = up ? t : lo;
+    hi = up ? hi : t;
+    if (it == kRowSteps) break;
+    t = fmaf(static_cast<float>(2 * c - target2), h, t);
+    c = count_ge(v, t);
+    if (c == k) {
+      emit_ge(v, col, t, ov, oi);
+      return;
+    }
+    if constexpr (QC > 0) {
+      if (c > k && c <= kW) {
+        compact_and_search<Q, QC, IdxT>(v, k, lane, t, c, h, scratch, ov, oi);
+        return;
+      }
+    }
+  }
+  finish_by_keys(v, col, k, lo, hi, ov, oi);
+}
+
 template <int Q, bool FULL, int QC, typename IdxT>
 __device__ __forceinline__ void exact_row(const float (&vin)[Q],
                                           const SelectArgs& a, int lane,
@@ -478,7 +583,7 @@ __device__ __forceinline__ void exact_row(const float (&vin)[Q],
   float v[Q];
   // Root mean square of the row: the scale of the model behind the
   // thresholds (the model assumes rows centred near zero; the Newton steps
-  // below correct the first threshold when they are not).
+  // correct the first threshold when they are not).
   float s2 = 0.0f;
 #pragma unroll
   for (int s = 0; s < Q; ++s) {
@@ -494,62 +599,20 @@ __device__ __forceinline__ void exact_row(const float (&vin)[Q],
   // Raw hardware square root: the model only steers the search.
   const float rms = __builtin_amdgcn_sqrtf(s2 * a.inv_m);
   const float h = rms * a.half_step_per_sd;
-  float t = rms * a.z_first;
-  float lo = -kInf, hi = kInf;
-  // Counts aimed at: the middle of (k, W] while looking for candidates,
-  // k + 1/2 otherwise (doubled to stay integral).
-  constexpr int kW = kWave * QC;
-  const int target2 = QC > 0 ? k + kW : 2 * k + 1;
-  auto col = [lane](int s) { return s * kWave + lane; };
-  int c;
-#pragma unroll 1
-  for (int it = 0;;) {
-    c = count_ge(v, t);
-    if (c == k || (QC > 0 && c > k && c <= kW) || ++it == kRowSteps) break;
-    const bool up = c > k;
-    lo = up ? t : lo;
-    hi = up ? hi : t;
-    t = fmaf(static_cast<float>(2 * c - target2), h, t);
-  }
-  if (c == k) {
-    emit_ge(v, col, t, ov, oi);
-    return;
-  }
+  const float t = rms * a.z_first;
+  const int c = count_ge(v, t);
   if constexpr (QC > 0) {
-    if (c > k && c <= kW) {
-      // Compact {x >= t} (every element the result can hold) into LDS in
-      // column order as (value bits, column) pairs; read back QC slots.
-      uint32_t base = 0;
-#pragma unroll
-      for (int s = 0; s < Q; ++s) {
-        const uint64_t msk = ballot(v[s] >= t);
-        if (__builtin_amdgcn_inverse_ballot_w64(msk)) {
-          scratch[rank_below(msk, base)] =
-              make_uint2(__float_as_uint(v[s]), static_cast<uint32_t>(col(s)));
-        }
-        base += popc(msk);
-      }
-      // LDS operations of one wave complete in issue order; the barrier
-      // only keeps the compiler from moving the reads above the writes.
-      __builtin_amdgcn_wave_barrier();
-      float cv[QC];
-      int ci[QC];
-#pragma unroll
-      for (int j = 0; j < QC; ++j) {
-        const int e = j * kWave + lane;
-        const uint2 w = scratch[e];
-        cv[j] = e < c ? __uint_as_float(w.x) : -kInf;
-        ci[j] = static_cast<int>(w.y);
-      }
-      __builtin_amdgcn_wave_barrier();
-      exact_candidates<QC>(cv, ci, k, t, c, h, ov, oi);
+    // c in (k, W], as one unsigned compare.
+    if (static_cast<uint32_t>(c - k - 1) < static_cast<uint32_t>(kWave * QC - k)) {
+      compact_and_search<Q, QC, IdxT>(v, k, lane, t, c, h, scratch, ov, oi);
       return;
     }
   }
-  const bool up = c > k;
-  lo = up ? t : lo;
-  hi = up ? hi : t;
-  finish_by_keys(v, col, k, lo, hi, ov, oi);
+  if (c == k) {
+    emit_ge(v, [lane](int s) { return s * kWave + lane; }, t, ov, oi);
+    return;
+  }
+  exact_row_search<Q, QC, IdxT>(v, k, lane, t, c, h, scratch, ov, oi);
 }
 
 // ---------------------------------------------------------------------------
@@ -582,8 +645,9 @@ constexpr int prefetch_depth() {
 // contiguous stretch of the matrix (HBM streams fastest that way).
 template <int Q, bool FULL, Mode MODE, int QC, typename IdxT>
 __global__ __launch_bounds__(kBlock) void rows_in_registers(SelectArgs a) {
-  // Per wave: room for 64*QC compacted (value, column) candidates.
-  constexpr int kScratch = (MODE == Mode::kExact && QC > 0) ? kWave * QC : 1;
+  // Per wave: room for 64*QC compacted (value, column) candidates
+  // (plus one spare entry per lane for the non-candidates' writes).
+  constexpr int kScratch = (MODE == Mode::kExact && QC > 0) ? kWave * (QC + 1) : 1;
   constexpr int D = prefetch_depth<Q>();
   __shared__ uint2 scratch_all[kWavesPerBlock][kScratch];
   const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
