@@ -30,6 +30,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "rows/sec and achieved HBM GB/s (% of peak), N=262144 M=256 k=32 fp32"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["rtopk_rows.hpp", "rtopk_dispatch.hip", "rtopk_internal.h"]
+COPY_REF_BYTES = 2**28
 
 
 def kernel_source_hash() -> str:
@@ -54,6 +55,59 @@ def measured_traffic(workload: str):
     return float(rec["bytes_per_launch"])
 
 
+def _counter_means(csv_path: str, counter: str):
+    """Mean per-dispatch value of one counter for the select kernel and for
+    the negation kernel, from a rocprofv3 counter_collection.csv."""
+    import csv
+    sel, ref = [], []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            if "rows_in_registers" in name:
+                sel.append(float(r["Counter_Value"]))
+            elif "neg" in name.lower():
+                ref.append(float(r["Counter_Value"]))
+    if not sel or not ref:
+        raise SystemExit(f"{csv_path}: no {counter} records for the select "
+                         "kernel or the negation reference")
+    return sum(sel) / len(sel), sum(ref) / len(ref)
+
+
+def record_traffic(workload: str, fetch_csv: str, write_csv: str) -> None:
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per
+    dispatch) of `bench.py --copy-reference` into HBM bytes per launch. Each
+    counter is scaled by the bytes the negation kernel is known to move
+    divided by what the same counter reads for it."""
+    f_sel, f_ref = _counter_means(fetch_csv, "FETCH_SIZE")
+    w_sel, w_ref = _counter_means(write_csv, "WRITE_SIZE")
+    f_scale = COPY_REF_BYTES / (f_ref * 1024.0)
+    w_scale = COPY_REF_BYTES / (w_ref * 1024.0)
+    fetched = f_sel * 1024.0 * f_scale
+    written = w_sel * 1024.0 * w_scale
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    data[workload] = {"kernel_hash": kernel_source_hash(),
+                      "bytes_per_launch": fetched + written,
+                      "fetch_bytes": fetched, "write_bytes": written,
+                      "fetch_kib_raw": f_sel, "write_kib_raw": w_sel,
+                      "fetch_scale": f_scale, "write_scale": w_scale}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(data[workload]))
+
+
+def workload_name(args) -> str:
+    return (f"{args.inputs} N={args.rows} M={args.m} k={args.k} {args.mode}"
+            + ("" if args.mode == "exact" else f" max_iter={args.max_iter} eps={args.eps}")
+            + f" idx={args.index}")
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -71,9 +125,12 @@ def parse():
                    help="input buffers to rotate (0: enough to exceed 768 MB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time for the oracle baseline (0: skip)")
+    p.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="write profiles/traffic.json for this workload from two "
+                        "rocprofv3 counter_collection.csv files and exit")
     p.add_argument("--copy-reference", action="store_true",
-                   help="after timing, run a plain 256 MiB device copy so that a "
-                        "counter run can calibrate FETCH_SIZE / WRITE_SIZE")
+                   help="after timing, run a plain 256 MiB streaming kernel so that "
+                        "a counter run can calibrate FETCH_SIZE / WRITE_SIZE")
     return p.parse_args()
 
 
@@ -84,6 +141,9 @@ def main():
               "supported (rows are independent: a multi-GPU run would give each "
               "GPU its own block of rows with no exchange).", file=sys.stderr)
         sys.exit(2)
+    if args.record_traffic:
+        record_traffic(workload_name(args), *args.record_traffic)
+        return
 
     import numpy as np
     import torch
@@ -142,20 +202,19 @@ def main():
     avg_launch_ms = ms_per_step
 
     if args.copy_reference:
-        # Plain copy of known size (268,435,456 bytes read and written).
-        src = torch.empty(2**26, dtype=torch.float32, device=dev).fill_(1.0)
+        # Plain streaming kernel of known size for scaling the HBM counters:
+        # an elementwise negation reads and writes 268,435,456 bytes each.
+        src = torch.ones(COPY_REF_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
 
     idx_bytes = 1 if u8 else 4
     per_row = 4 * m + k * (4 + idx_bytes)
     algo_bytes = n * per_row
     achieved = algo_bytes / (avg_launch_ms * 1e-3) / 1e9
-    workload = (f"{args.inputs} N={n} M={m} k={k} {args.mode}"
-                + ("" if args.mode == "exact" else f" max_iter={args.max_iter} eps={args.eps}")
-                + f" idx={args.index}")
+    workload = workload_name(args)
     traffic = measured_traffic(workload)
 
     cpu = None

@@ -30,7 +30,7 @@ rtopk_status_t run(const float* x, int64_t n, int32_t m, int32_t k,
       validate(x, n, m, k, eps, out_val, out_idx, u8_index);
   if (st != RTOPK_SUCCESS) return st;
   if (n == 0) return RTOPK_SUCCESS;
-  rtopk::SelectArgs a{x, n, m, k, max_iter, eps, out_val, out_idx, 0.0f, 0.0f, 0.0f};
+  rtopk::SelectArgs a{x, n, m, k, max_iter, eps, out_val, out_idx, 0.0f, 0.0f};
   const hipError_t err = rtopk::launch_select(a, mode, u8_index, stream);
   return err == hipSuccess ? RTOPK_SUCCESS : RTOPK_ERROR_LAUNCH;
 }

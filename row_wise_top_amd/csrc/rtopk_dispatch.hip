@@ -105,9 +105,10 @@ void exact_model(SelectArgs& a, int qc) {
   const double first = qc > 0 ? 0.5 * (a.k + kWave * qc) : a.k + 0.5;
   const double z_first = normal_upper_quantile(frac(first));
   const double z_k = normal_upper_quantile(frac(a.k + 0.5));
-  a.inv_m = static_cast<float>(1.0 / m);
-  a.z_first = static_cast<float>(z_first);
-  a.half_step_per_sd = static_cast<float>(0.5 / (m * normal_density(z_k)));
+  // The kernel has r = sqrt(sum x^2) = rms * sqrt(m); fold 1/sqrt(m) in.
+  const double inv_sqrt_m = 1.0 / std::sqrt(m);
+  a.z_first = static_cast<float>(z_first * inv_sqrt_m);
+  a.half_step = static_cast<float>(0.5 / (m * normal_density(z_k)) * inv_sqrt_m);
 }
 
 }  // namespace

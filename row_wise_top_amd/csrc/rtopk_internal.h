@@ -27,9 +27,9 @@ struct SelectArgs {
   void* out_idx;     // int32_t* or uint8_t*
   // Exact search only: thresholds from a normal model of the row (host
   // computed; they steer the search, never its result).
-  float inv_m;             // 1 / m
-  float z_first;           // first threshold = mean + z_first * sd
-  float half_step_per_sd;  // Newton step per doubled count, in units of sd
+  // With r = sqrt(sum of squares of the row) = rms * sqrt(m):
+  float z_first;     // first threshold = r * z_first
+  float half_step;   // Newton step per doubled count = r * half_step
 };
 
 using RowsKernel = void (*)(SelectArgs);

@@ -442,8 +442,9 @@ __device__ __forceinline__ void settle_candidates(const float (&cv)[QC],
 // The candidates left after compaction: QC slots in column order (unused
 // lanes hold -inf), all elements >= t0, with c0 = #{x >= t0} in (k, 64*QC].
 // A fixed number of Newton steps toward k + 1/2 elements runs straight
-// through (no bracket bookkeeping); a count of exactly k ends it. Otherwise
-// the bracket is rebuilt from the recorded steps and the row is settled.
+// through; a count of exactly k ends the row right there (the emission uses
+// the compares of that count). Otherwise the row is settled from the bracket
+// given by the start and the last step.
 template <int QC, typename IdxT>
 __device__ __forceinline__ void exact_candidates(const float (&cv)[QC],
                                                  const int (&ci)[QC], int k,
@@ -452,99 +453,98 @@ __device__ __forceinline__ void exact_candidates(const float (&cv)[QC],
                                                  IdxT* __restrict__ oi) {
   auto col = [&ci](int s) { return ci[s]; };
   const int target2 = 2 * k + 1;
-  float ts[kCandSteps];
-  int cs[kCandSteps];
   float t = t0;
   int c = c0;
-  int steps = 0;
 #pragma unroll
   for (int i = 0; i < kCandSteps; ++i) {
     t = fmaf(static_cast<float>(2 * c - target2), h, t);
     c = count_ge(cv, t);
-    ts[i] = t;
-    cs[i] = c;
-    steps = i + 1;
-    if (c == k) break;
-  }
-  if (c == k) {
-    emit_ge(cv, col, t, ov, oi);
-    return;
-  }
-  // Tightest bracket seen: every count gave a valid bound.
-  float lo = t0, hi = kInf;
-  int clo = c0, chi = 0;
-#pragma unroll
-  for (int i = 0; i < kCandSteps; ++i) {
-    if (i < steps) {
-      if (cs[i] > k && ts[i] > lo) {
-        lo = ts[i];
-        clo = cs[i];
-      }
-      if (cs[i] < k && ts[i] < hi) {
-        hi = ts[i];
-        chi = cs[i];
-      }
+    if (c == k) {
+      emit_ge(cv, col, t, ov, oi);
+      return;
     }
   }
-  settle_candidates<QC>(cv, col, k, lo, clo, hi, chi, ov, oi);
+  // Both ends are valid bounds (every count is).
+  const bool up = c > k;
+  settle_candidates<QC>(cv, col, k, up ? t : t0, up ? c : c0, up ? kInf : t,
+                        up ? 0 : c, ov, oi);
+}
+
+// Whether the LDS staging area of a wave holds a whole row (64*Q entries):
+// then candidates are written under an exec mask with no capacity check.
+template <int Q>
+constexpr bool stage_whole_row() {
+  return Q <= 8;
+}
+
+// LDS staging entries per wave for the exact search with QC candidate slots.
+template <int Q, int QC>
+constexpr int stage_entries() {
+  return stage_whole_row<Q>() ? kWave * Q : kWave * (QC + 1);
+}
+
+// Count {x >= t} over the row and, in the same pass, write those elements
+// into LDS in column order: value bits at entry e, the column at entry
+// E + e, E = stage_entries (two separate words, so no register pairing).
+// The staging is only used when the count lands in (k, 64*QC]. When the
+// area cannot hold a whole row, positions past the candidate capacity 64*QC
+// and lanes whose element is below t write the lane's spare entry
+// 64*QC + lane instead (never read).
+template <int Q, int QC>
+__device__ __forceinline__ int count_and_stage(const float (&v)[Q], float t,
+                                               int lane,
+                                               uint32_t* __restrict__ scratch) {
+  constexpr uint32_t kW = kWave * QC;
+  constexpr uint32_t kE = stage_entries<Q, QC>();
+  const uint32_t spare = kW + static_cast<uint32_t>(lane);
+  uint32_t base = 0;
+#pragma unroll
+  for (int s = 0; s < Q; ++s) {
+    const bool p = v[s] >= t;
+    const uint64_t msk = ballot(p);
+    if constexpr (stage_whole_row<Q>()) {
+      if (p) {
+        const uint32_t e = rank_below(msk, base);
+        scratch[e] = __float_as_uint(v[s]);
+        scratch[kE + e] = static_cast<uint32_t>(s * kWave + lane);
+      }
+    } else {
+      const uint32_t e = min(p ? rank_below(msk, base) : spare, spare);
+      scratch[e] = __float_as_uint(v[s]);
+      scratch[kE + e] = static_cast<uint32_t>(s * kWave + lane);
+    }
+    base += popc(msk);
+  }
+  return static_cast<int>(base);
+}
+
+// Read back the staged candidates (c of them) into QC slots.
+template <int Q, int QC>
+__device__ __forceinline__ void read_candidates(const uint32_t* __restrict__ scratch,
+                                                int c, int lane, float (&cv)[QC],
+                                                int (&ci)[QC]) {
+  constexpr int kE = stage_entries<Q, QC>();
+  // LDS operations of one wave complete in issue order; the barriers only
+  // keep the compiler from moving these reads across the writes.
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int j = 0; j < QC; ++j) {
+    const int e = j * kWave + lane;
+    const float x = __uint_as_float(scratch[e]);
+    cv[j] = e < c ? x : -kInf;
+    ci[j] = static_cast<int>(scratch[kE + e]);
+  }
+  __builtin_amdgcn_wave_barrier();
 }
 
 // Full-row search when the first count missed the candidate window: Newton
 // steps on the whole row (compacting as soon as a count lands in (k, W]),
 // then order-key bisection.
 template <int Q, int QC, typename IdxT>
-__device__ __noinline__ void exact_row_search(const float (&v)[Q], int k,
+__device__ __forceinline__ void exact_row_search(const float (&v)[Q], int k,
                                               int lane, float t, int c,
                                               float h,
-                                              uint2* __restrict__ scratch,
-                                              float* __restrict__ ov,
-                                              IdxT* __restrict__ oi);
-
-template <int Q, int QC, typename IdxT>
-__device__ __forceinline__ void compact_and_search(const float (&v)[Q], int k,
-                                                   int lane, float t, int c,
-                                                   float h,
-                                                   uint2* __restrict__ scratch,
-                                                   float* __restrict__ ov,
-                                                   IdxT* __restrict__ oi) {
-  // Compact {x >= t} (every element the result can hold) into LDS in
-  // column order as (value bits, column) pairs. Lanes whose element is not
-  // a candidate write a per-lane spare entry instead, so the writes need no
-  // exec-mask switching.
-  constexpr int kW = kWave * QC;
-  uint32_t base = 0;
-#pragma unroll
-  for (int s = 0; s < Q; ++s) {
-    const uint64_t msk = ballot(v[s] >= t);
-    const uint32_t pos = rank_below(msk, base);
-    const uint32_t e = __builtin_amdgcn_inverse_ballot_w64(msk)
-                           ? pos
-                           : static_cast<uint32_t>(kW + lane);
-    scratch[e] = make_uint2(__float_as_uint(v[s]),
-                            static_cast<uint32_t>(s * kWave + lane));
-    base += popc(msk);
-  }
-  // LDS operations of one wave complete in issue order; the barrier only
-  // keeps the compiler from moving the reads above the writes.
-  __builtin_amdgcn_wave_barrier();
-  float cv[QC];
-  int ci[QC];
-#pragma unroll
-  for (int j = 0; j < QC; ++j) {
-    const int e = j * kWave + lane;
-    const uint2 w = scratch[e];
-    cv[j] = e < c ? __uint_as_float(w.x) : -kInf;
-    ci[j] = static_cast<int>(w.y);
-  }
-  __builtin_amdgcn_wave_barrier();
-  exact_candidates<QC>(cv, ci, k, t, c, h, ov, oi);
-}
-
-template <int Q, int QC, typename IdxT>
-__device__ __noinline__ void exact_row_search(const float (&v)[Q], int k,
-                                              int lane, float t, int c,
-                                              float h,
-                                              uint2* __restrict__ scratch,
+                                              uint32_t* __restrict__ scratch,
                                               float* __restrict__ ov,
                                               IdxT* __restrict__ oi) {
   constexpr int kW = kWave * QC;
@@ -565,7 +565,11 @@ __device__ __noinline__ void exact_row_search(const float (&v)[Q], int k,
     }
     if constexpr (QC > 0) {
       if (c > k && c <= kW) {
-        compact_and_search<Q, QC, IdxT>(v, k, lane, t, c, h, scratch, ov, oi);
+        count_and_stage<Q, QC>(v, t, lane, scratch);
+        float cv[QC];
+        int ci[QC];
+        read_candidates<Q, QC>(scratch, c, lane, cv, ci);
+        exact_candidates<QC>(cv, ci, k, t, c, h, ov, oi);
         return;
       }
     }
@@ -576,14 +580,14 @@ __device__ __noinline__ void exact_row_search(const float (&v)[Q], int k,
 template <int Q, bool FULL, int QC, typename IdxT>
 __device__ __forceinline__ void exact_row(const float (&vin)[Q],
                                           const SelectArgs& a, int lane,
-                                          uint2* __restrict__ scratch,
+                                          uint32_t* __restrict__ scratch,
                                           float* __restrict__ ov,
                                           IdxT* __restrict__ oi) {
   const int k = a.k;
   float v[Q];
-  // Root mean square of the row: the scale of the model behind the
-  // thresholds (the model assumes rows centred near zero; the Newton steps
-  // correct the first threshold when they are not).
+  // Scale of the row for the model behind the thresholds (the model assumes
+  // rows centred near zero; the Newton steps correct the first threshold
+  // when they are not).
   float s2 = 0.0f;
 #pragma unroll
   for (int s = 0; s < Q; ++s) {
@@ -592,21 +596,27 @@ __device__ __forceinline__ void exact_row(const float (&vin)[Q],
     s2 = fmaf(x, x, s2);
   }
   s2 = wave_sum(s2);
-  // Squares of values beyond ~1.8e19 overflow: give up on the model then
-  // (thresholds stay finite and the order-key bisection does the work).
-  s2 = s2 < kInf ? s2 : 0.0f;
   mask_tail<Q, FULL>(a.m, lane, v);
-  // Raw hardware square root: the model only steers the search.
-  const float rms = __builtin_amdgcn_sqrtf(s2 * a.inv_m);
-  const float h = rms * a.half_step_per_sd;
-  const float t = rms * a.z_first;
-  const int c = count_ge(v, t);
+  // r = sqrt(sum of squares) = rms * sqrt(m); the host folded 1/sqrt(m) into
+  // the model constants. Raw hardware square root: the model only steers
+  // the search. Squares beyond ~1.8e19 overflow to +inf: clamping r keeps
+  // every threshold finite (the search then relies on its bounded fallbacks).
+  const float r = fminf(__builtin_amdgcn_sqrtf(s2), 3.0e38f);
+  const float h = r * a.half_step;
+  const float t = r * a.z_first;
+  int c;
   if constexpr (QC > 0) {
+    c = count_and_stage<Q, QC>(v, t, lane, scratch);
     // c in (k, W], as one unsigned compare.
     if (static_cast<uint32_t>(c - k - 1) < static_cast<uint32_t>(kWave * QC - k)) {
-      compact_and_search<Q, QC, IdxT>(v, k, lane, t, c, h, scratch, ov, oi);
+      float cv[QC];
+      int ci[QC];
+      read_candidates<Q, QC>(scratch, c, lane, cv, ci);
+      exact_candidates<QC>(cv, ci, k, t, c, h, ov, oi);
       return;
     }
+  } else {
+    c = count_ge(v, t);
   }
   if (c == k) {
     emit_ge(v, [lane](int s) { return s * kWave + lane; }, t, ov, oi);
@@ -621,7 +631,7 @@ __device__ __forceinline__ void exact_row(const float (&vin)[Q],
 template <int Q, bool FULL, Mode MODE, int QC, typename IdxT>
 __device__ __forceinline__ void process_row(const float (&v)[Q],
                                             const SelectArgs& a, int lane,
-                                            uint2* __restrict__ scratch,
+                                            uint32_t* __restrict__ scratch,
                                             float* __restrict__ ov,
                                             IdxT* __restrict__ oi) {
   if constexpr (MODE == Mode::kExact)
@@ -633,10 +643,14 @@ __device__ __forceinline__ void process_row(const float (&v)[Q],
 // Rows each wave keeps in flight: the row being worked on plus D - 1
 // prefetched ones. The prefetch loads are unconditional (past the last row
 // they re-read it) so that the compiler's wait counts stay exact and a
-// wave only ever waits for the row it is about to use.
+// wave only ever waits for the row it is about to use. Two rows in flight
+// per wave, at the full occupancy the register budget allows for short
+// rows, streamed faster than three rows at fewer waves: more waves hide the
+// search's issue latency, and one extra row per wave already covers the
+// load latency.
 template <int Q>
 constexpr int prefetch_depth() {
-  return Q <= 4 ? 3 : (Q <= 16 ? 2 : 1);
+  return Q <= 16 ? 2 : 1;
 }
 
 // Row order. Wave w of S works through groups of D consecutive rows:
@@ -645,45 +659,56 @@ constexpr int prefetch_depth() {
 // contiguous stretch of the matrix (HBM streams fastest that way).
 template <int Q, bool FULL, Mode MODE, int QC, typename IdxT>
 __global__ __launch_bounds__(kBlock) void rows_in_registers(SelectArgs a) {
-  // Per wave: room for 64*QC compacted (value, column) candidates
-  // (plus one spare entry per lane for the non-candidates' writes).
-  constexpr int kScratch = (MODE == Mode::kExact && QC > 0) ? kWave * (QC + 1) : 1;
+  // Per wave: the LDS staging area of the exact search, (value, column)
+  // pairs (see stage_entries).
+  constexpr int kScratch = (MODE == Mode::kExact && QC > 0) ? 2 * stage_entries<Q, QC>() : 1;
   constexpr int D = prefetch_depth<Q>();
-  __shared__ uint2 scratch_all[kWavesPerBlock][kScratch];
+  __shared__ uint32_t scratch_all[kWavesPerBlock][kScratch];
   const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
   const int wave_in_block =
       __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-  uint2* scratch = scratch_all[wave_in_block];
+  uint32_t* scratch = scratch_all[wave_in_block];
   const int64_t waves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
   const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_in_block;
   int64_t r = w * D;  // first row of the current group
   if (r >= a.n) return;
+  // Rows this wave will process: D per full group of D*waves rows, plus the
+  // part of its last group before the end (at least one row: r < n).
+  const int64_t group_rows = waves * D;
+  int rows_left;
+  {
+    const int64_t rem = a.n - r;
+    const int64_t g = rem / group_rows;
+    const int64_t tail = rem - g * group_rows;
+    const int64_t total = g * D + (tail < D ? tail : D);
+    rows_left = total < 0x7fffffff ? static_cast<int>(total) : 0x7fffffff;
+  }
   // Pointers advance by constant steps (no per-row 64-bit multiply).
   const int64_t m = a.m, k = a.k;
-  const float* const x_last = a.x + (a.n - 1) * m;
-  const int64_t group_rows = waves * D;
   const float* xg = a.x + r * m;  // current group
   float* og = a.out_val + r * k;
   IdxT* ig = static_cast<IdxT*>(a.out_idx) + r * k;
   float buf[D][Q];
+  // Unconditional loads (rows past this wave's last one re-read its last
+  // row) so that the compiler's wait counts need no worst-case assumption.
 #pragma unroll
-  for (int d = 0; d + 1 < D; ++d) {
-    const float* p = xg + d * m;
-    load_row<Q, FULL>(p < x_last ? p : x_last, a.m, lane, buf[d]);
-  }
+  for (int d = 0; d + 1 < D; ++d)
+    load_row<Q, FULL>(xg + min(d, rows_left - 1) * m, a.m, lane, buf[d]);
   for (;;) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       // buf[d] holds row r + d. Refill the buffer freed by the previous row
-      // with the row D - 1 places further on in this wave's order.
+      // with the row D - 1 places further on in this wave's order (or, past
+      // its last row, re-read the current group's first row: a valid row).
       const float* p = d == 0 ? xg + (D - 1) * m : xg + (group_rows + d - 1) * m;
-      load_row<Q, FULL>(p < x_last ? p : x_last, a.m, lane, buf[(d + D - 1) % D]);
-      if (r + d >= a.n) return;
+      load_row<Q, FULL>(d + D - 1 < rows_left ? p : xg, a.m, lane,
+                        buf[(d + D - 1) % D]);
+      if (d >= rows_left) return;
       process_row<Q, FULL, MODE, QC, IdxT>(buf[d], a, lane, scratch, og + d * k,
                                            ig + d * k);
     }
-    r += group_rows;
-    if (r >= a.n) return;
+    rows_left -= D;
+    if (rows_left <= 0) return;
     xg += group_rows * m;
     og += group_rows * k;
     ig += group_rows * k;
