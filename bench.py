@@ -6,7 +6,10 @@ one-byte column indices (the compressed balanced layout of a MaxK
 nonlinearity), rows = N(0,1) x per-row scale U(0.5,2) with 5% exact zeros
 (workloads.py). One step = one call of the library over the whole batch.
 Inputs rotate over several resident buffers so that the 256 MB last-level
-cache cannot serve them; everything is in HBM before timing starts.
+cache cannot serve them; everything is in HBM before timing starts. From
+idle, launch times drift by up to 25% over the first ~150 launches while the
+GPU's power management settles, so the default run warms up with 300 untimed
+launches and then times 300.
 
 Prints one JSON line: rows/s (whole job), the kernel's achieved algorithmic
 HBM bandwidth against the 8 TB/s peak (roofline), the HBM traffic measured by
@@ -111,8 +114,10 @@ def workload_name(args) -> str:
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=300)
+    p.add_argument("--warmup", type=int, default=300,
+                   help="untimed launches first; the GPU's clocks take about "
+                        "150 launches (~10 ms) of sustained load to settle")
     p.add_argument("--rows", type=int, default=262144)
     p.add_argument("--m", type=int, default=256)
     p.add_argument("--k", type=int, default=32)

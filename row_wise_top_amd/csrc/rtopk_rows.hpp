@@ -66,6 +66,16 @@ __device__ __forceinline__ uint64_t ballot(bool p) {
 
 __device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
 
+// (bit `lane` of mask) ? a : b, as one v_cndmask. Written out because the
+// compiler turns a select whose operand is only needed on one side into an
+// exec-masked region (two scalar instructions to save and restore exec).
+__device__ __forceinline__ uint32_t lane_select(uint64_t mask, uint32_t a,
+                                                uint32_t b) {
+  uint32_t r;
+  asm("v_cndmask_b32_e64 %0, %2, %1, %3" : "=v"(r) : "v"(a), "v"(b), "s"(mask));
+  return r;
+}
+
 // Cross-lane read through DPP, all rows and banks enabled. A lane whose
 // source does not exist (row 0 for the row broadcasts) reads 0 (bound_ctrl);
 // the reductions below only use lane 63, whose sources always exist.
@@ -190,37 +200,52 @@ __device__ __forceinline__ float key_value(int32_t key) {
 }
 
 // ---------------------------------------------------------------------------
-// Emission. Both write exactly k entries, in column order.
+// Emission. Every emission writes exactly k entries, in column order.
 // `col(s)` gives the column held by slot s of the calling lane.
+//
+// The two output rows are addressed as buffer resources whose size is the
+// row's k entries. A buffer store at an offset past that size is discarded
+// by the hardware, so every lane stores and the lanes not selected use a
+// position past the end: the stores need no exec-mask changes and the
+// compiler's wait counts stay exact.
 // ---------------------------------------------------------------------------
 
-// Every element >= t; the caller has counted exactly k of them.
-template <int S, typename IdxT, typename ColFn>
-__device__ __forceinline__ void emit_at_threshold(const float (&v)[S],
-                                                  ColFn col, float t,
-                                                  float* __restrict__ ov,
-                                                  IdxT* __restrict__ oi) {
-  uint32_t base = 0;
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const bool p = v[s] >= t;
-    const uint64_t msk = ballot(p);
-    if (p) {
-      const uint32_t pos = rank_below(msk, base);
-      ov[pos] = v[s];
-      oi[pos] = static_cast<IdxT>(col(s));
+// Word 3 of a gfx9 buffer resource for untyped 32-bit access (data format 32).
+constexpr int kRsrcWord3 = 0x00020000;
+// Output position of a lane that stores nothing: past any row end, and times
+// four still a valid 32-bit offset.
+constexpr uint32_t kDropPos = 1u << 28;
+
+template <typename IdxT>
+struct OutRow {
+  __amdgpu_buffer_rsrc_t val;
+  __amdgpu_buffer_rsrc_t idx;
+
+  __device__ __forceinline__ OutRow(float* ov, IdxT* oi, int k)
+      : val(__builtin_amdgcn_make_buffer_rsrc(ov, 0, k * 4, kRsrcWord3)),
+        idx(__builtin_amdgcn_make_buffer_rsrc(
+            oi, 0, k * static_cast<int>(sizeof(IdxT)), kRsrcWord3)) {}
+
+  // Entry `pos` of the row gets (x, col); pos == kDropPos stores nothing.
+  __device__ __forceinline__ void put(uint32_t pos, float x, int col) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), val,
+                                          static_cast<int>(pos * 4u), 0, 0);
+    if constexpr (sizeof(IdxT) == 1) {
+      __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(col), idx,
+                                           static_cast<int>(pos), 0, 0);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(col), idx,
+                                            static_cast<int>(pos * 4u), 0, 0);
     }
-    base += popc(msk);
   }
-}
+};
 
 // The second pass: the first k (by column) of A = {x >= hi}, then of
 // B = {lo <= x < hi}. Requires #{x >= lo} >= k.
 template <int S, typename IdxT, typename ColFn>
 __device__ __forceinline__ void emit_fill(const float (&v)[S], ColFn col,
                                           float lo, float hi, int k,
-                                          float* __restrict__ ov,
-                                          IdxT* __restrict__ oi) {
+                                          const OutRow<IdxT>& out) {
   int nA = 0;
 #pragma unroll
   for (int s = 0; s < S; ++s) nA += popc(ballot(v[s] >= hi));
@@ -252,13 +277,8 @@ __device__ __forceinline__ void emit_fill(const float (&v)[S], ColFn col,
         selB = b && static_cast<int>(rank_below(mB, accB)) < needB;
       accB += pb;
     }
-    const bool sel = selA || selB;
-    const uint64_t mS = ballot(sel);
-    if (sel) {
-      const uint32_t pos = rank_below(mS, base);
-      ov[pos] = v[s];
-      oi[pos] = static_cast<IdxT>(col(s));
-    }
+    const uint64_t mS = ballot(selA || selB);
+    out.put(lane_select(mS, rank_below(mS, base), kDropPos), v[s], col(s));
     base += popc(mS);
   }
 }
@@ -270,8 +290,7 @@ __device__ __forceinline__ void emit_fill(const float (&v)[S], ColFn col,
 template <int Q, bool FULL, typename IdxT>
 __device__ __forceinline__ void capped_row(const float (&vin)[Q],
                                            const SelectArgs& a, int lane,
-                                           float* __restrict__ ov,
-                                           IdxT* __restrict__ oi) {
+                                           const OutRow<IdxT>& out) {
   float v[Q];
   float mn = kInf, mx = -kInf;
 #pragma unroll
@@ -301,7 +320,7 @@ __device__ __forceinline__ void capped_row(const float (&vin)[Q],
     lo = up ? mid : lo;
     hi = up ? hi : mid;
   }
-  emit_fill(v, [lane](int s) { return s * kWave + lane; }, lo, hi, k, ov, oi);
+  emit_fill(v, [lane](int s) { return s * kWave + lane; }, lo, hi, k, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -347,21 +366,15 @@ __device__ __forceinline__ float next_float(float f) {
 }
 
 // Every element >= t (the caller has counted exactly k), in column order.
-// The lane masks come straight from the compares, so the stores run under
-// exec = mask without re-deriving the predicate.
+// The lane masks come straight from the compares and select the positions.
 template <int S, typename IdxT, typename ColFn>
 __device__ __forceinline__ void emit_ge(const float (&v)[S], ColFn col,
-                                        float t, float* __restrict__ ov,
-                                        IdxT* __restrict__ oi) {
+                                        float t, const OutRow<IdxT>& out) {
   uint32_t base = 0;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const uint64_t msk = ballot(v[s] >= t);
-    if (__builtin_amdgcn_inverse_ballot_w64(msk)) {
-      const uint32_t pos = rank_below(msk, base);
-      ov[pos] = v[s];
-      oi[pos] = static_cast<IdxT>(col(s));
-    }
+    out.put(lane_select(msk, rank_below(msk, base), kDropPos), v[s], col(s));
     base += popc(msk);
   }
 }
@@ -371,8 +384,7 @@ __device__ __forceinline__ void emit_ge(const float (&v)[S], ColFn col,
 template <int S, typename IdxT, typename ColFn>
 __device__ __forceinline__ void finish_by_keys(const float (&v)[S], ColFn col,
                                                int k, float lo, float hi,
-                                               float* __restrict__ ov,
-                                               IdxT* __restrict__ oi) {
+                                               const OutRow<IdxT>& out) {
   int32_t klo = order_key(lo);
   int32_t khi = order_key(hi);
 #pragma unroll 1
@@ -384,14 +396,14 @@ __device__ __forceinline__ void finish_by_keys(const float (&v)[S], ColFn col,
     const float t = key_value(kmid);
     const int c = count_ge(v, t);
     if (c == k) {
-      emit_ge(v, col, t, ov, oi);
+      emit_ge(v, col, t, out);
       return;
     }
     const bool up = c > k;
     klo = up ? kmid : klo;
     khi = up ? khi : kmid;
   }
-  emit_fill(v, col, key_value(klo), key_value(khi), k, ov, oi);
+  emit_fill(v, col, key_value(klo), key_value(khi), k, out);
 }
 
 // Snaps, then order-key bisection, on the candidates once the Newton steps
@@ -403,8 +415,7 @@ template <int QC, typename IdxT, typename ColFn>
 __device__ __forceinline__ void settle_candidates(const float (&cv)[QC],
                                                   ColFn col, int k, float lo,
                                                   int clo, float hi, int chi,
-                                                  float* __restrict__ ov,
-                                                  IdxT* __restrict__ oi) {
+                                                  const OutRow<IdxT>& out) {
 #pragma unroll 1
   for (int it = 0; it < kCandSnaps; ++it) {
     const int need = k - chi;           // survivors still to take from [lo, hi)
@@ -416,7 +427,7 @@ __device__ __forceinline__ void settle_candidates(const float (&cv)[QC],
       u = wave_max(u);
       const int cu = count_ge(cv, u);
       if (cu >= k) {
-        emit_fill(cv, col, u, hi, k, ov, oi);
+        emit_fill(cv, col, u, hi, k, out);
         return;
       }
       hi = u;
@@ -429,14 +440,14 @@ __device__ __forceinline__ void settle_candidates(const float (&cv)[QC],
       const float above = next_float(u);
       const int cg = count_ge(cv, above);
       if (cg <= k) {
-        emit_fill(cv, col, u, above, k, ov, oi);
+        emit_fill(cv, col, u, above, k, out);
         return;
       }
       lo = above;
       clo = cg;
     }
   }
-  finish_by_keys(cv, col, k, lo, hi, ov, oi);
+  finish_by_keys(cv, col, k, lo, hi, out);
 }
 
 // The candidates left after compaction: QC slots in column order (unused
@@ -449,70 +460,68 @@ template <int QC, typename IdxT>
 __device__ __forceinline__ void exact_candidates(const float (&cv)[QC],
                                                  const int (&ci)[QC], int k,
                                                  float t0, int c0, float h,
-                                                 float* __restrict__ ov,
-                                                 IdxT* __restrict__ oi) {
+                                                 const OutRow<IdxT>& out) {
   auto col = [&ci](int s) { return ci[s]; };
-  const int target2 = 2 * k + 1;
+  // t + (2c - target2) h, as an fma on the count (vector arithmetic only).
+  const float h2 = 2.0f * h;
+  const float shift = -static_cast<float>(2 * k + 1) * h;
   float t = t0;
   int c = c0;
 #pragma unroll
   for (int i = 0; i < kCandSteps; ++i) {
-    t = fmaf(static_cast<float>(2 * c - target2), h, t);
+    t = fmaf(static_cast<float>(c), h2, t + shift);
     c = count_ge(cv, t);
     if (c == k) {
-      emit_ge(cv, col, t, ov, oi);
+      emit_ge(cv, col, t, out);
       return;
     }
   }
   // Both ends are valid bounds (every count is).
   const bool up = c > k;
   settle_candidates<QC>(cv, col, k, up ? t : t0, up ? c : c0, up ? kInf : t,
-                        up ? 0 : c, ov, oi);
+                        up ? 0 : c, out);
 }
 
-// Whether the LDS staging area of a wave holds a whole row (64*Q entries):
-// then candidates are written under an exec mask with no capacity check.
+// Whether the LDS staging area of a wave has room for a whole row (64*Q
+// entries): then a candidate's rank needs no capacity check.
 template <int Q>
 constexpr bool stage_whole_row() {
   return Q <= 8;
 }
 
+// Entries of the staging area that ranks can reach; 64 spare entries (one
+// per lane) follow them.
+template <int Q, int QC>
+constexpr int stage_reach() {
+  return stage_whole_row<Q>() ? kWave * Q : kWave * QC;
+}
+
 // LDS staging entries per wave for the exact search with QC candidate slots.
 template <int Q, int QC>
 constexpr int stage_entries() {
-  return stage_whole_row<Q>() ? kWave * Q : kWave * (QC + 1);
+  return stage_reach<Q, QC>() + kWave;
 }
 
 // Count {x >= t} over the row and, in the same pass, write those elements
 // into LDS in column order: value bits at entry e, the column at entry
 // E + e, E = stage_entries (two separate words, so no register pairing).
-// The staging is only used when the count lands in (k, 64*QC]. When the
-// area cannot hold a whole row, positions past the candidate capacity 64*QC
-// and lanes whose element is below t write the lane's spare entry
-// 64*QC + lane instead (never read).
+// The staging is only used when the count lands in (k, 64*QC]. Every lane
+// writes (no exec-mask changes): lanes whose element is below t, and ranks
+// past the reachable part, write the lane's spare entry (never read).
 template <int Q, int QC>
 __device__ __forceinline__ int count_and_stage(const float (&v)[Q], float t,
                                                int lane,
                                                uint32_t* __restrict__ scratch) {
-  constexpr uint32_t kW = kWave * QC;
   constexpr uint32_t kE = stage_entries<Q, QC>();
-  const uint32_t spare = kW + static_cast<uint32_t>(lane);
+  const uint32_t spare = stage_reach<Q, QC>() + static_cast<uint32_t>(lane);
   uint32_t base = 0;
 #pragma unroll
   for (int s = 0; s < Q; ++s) {
-    const bool p = v[s] >= t;
-    const uint64_t msk = ballot(p);
-    if constexpr (stage_whole_row<Q>()) {
-      if (p) {
-        const uint32_t e = rank_below(msk, base);
-        scratch[e] = __float_as_uint(v[s]);
-        scratch[kE + e] = static_cast<uint32_t>(s * kWave + lane);
-      }
-    } else {
-      const uint32_t e = min(p ? rank_below(msk, base) : spare, spare);
-      scratch[e] = __float_as_uint(v[s]);
-      scratch[kE + e] = static_cast<uint32_t>(s * kWave + lane);
-    }
+    const uint64_t msk = ballot(v[s] >= t);
+    uint32_t e = lane_select(msk, rank_below(msk, base), spare);
+    if constexpr (!stage_whole_row<Q>()) e = min(e, spare);
+    scratch[e] = __float_as_uint(v[s]);
+    scratch[kE + e] = static_cast<uint32_t>(s * kWave + lane);
     base += popc(msk);
   }
   return static_cast<int>(base);
@@ -545,10 +554,11 @@ __device__ __forceinline__ void exact_row_search(const float (&v)[Q], int k,
                                               int lane, float t, int c,
                                               float h,
                                               uint32_t* __restrict__ scratch,
-                                              float* __restrict__ ov,
-                                              IdxT* __restrict__ oi) {
+                                              const OutRow<IdxT>& out) {
   constexpr int kW = kWave * QC;
   const int target2 = QC > 0 ? k + kW : 2 * k + 1;
+  const float h2 = 2.0f * h;
+  const float shift = -static_cast<float>(target2) * h;
   auto col = [lane](int s) { return s * kWave + lane; };
   float lo = -kInf, hi = kInf;
 #pragma unroll 1
@@ -557,10 +567,10 @@ __device__ __forceinline__ void exact_row_search(const float (&v)[Q], int k,
     lo = up ? t : lo;
     hi = up ? hi : t;
     if (it == kRowSteps) break;
-    t = fmaf(static_cast<float>(2 * c - target2), h, t);
+    t = fmaf(static_cast<float>(c), h2, t + shift);
     c = count_ge(v, t);
     if (c == k) {
-      emit_ge(v, col, t, ov, oi);
+      emit_ge(v, col, t, out);
       return;
     }
     if constexpr (QC > 0) {
@@ -569,20 +579,19 @@ __device__ __forceinline__ void exact_row_search(const float (&v)[Q], int k,
         float cv[QC];
         int ci[QC];
         read_candidates<Q, QC>(scratch, c, lane, cv, ci);
-        exact_candidates<QC>(cv, ci, k, t, c, h, ov, oi);
+        exact_candidates<QC>(cv, ci, k, t, c, h, out);
         return;
       }
     }
   }
-  finish_by_keys(v, col, k, lo, hi, ov, oi);
+  finish_by_keys(v, col, k, lo, hi, out);
 }
 
 template <int Q, bool FULL, int QC, typename IdxT>
 __device__ __forceinline__ void exact_row(const float (&vin)[Q],
                                           const SelectArgs& a, int lane,
                                           uint32_t* __restrict__ scratch,
-                                          float* __restrict__ ov,
-                                          IdxT* __restrict__ oi) {
+                                          const OutRow<IdxT>& out) {
   const int k = a.k;
   float v[Q];
   // Scale of the row for the model behind the thresholds (the model assumes
@@ -599,9 +608,12 @@ __device__ __forceinline__ void exact_row(const float (&vin)[Q],
   mask_tail<Q, FULL>(a.m, lane, v);
   // r = sqrt(sum of squares) = rms * sqrt(m); the host folded 1/sqrt(m) into
   // the model constants. Raw hardware square root: the model only steers
-  // the search. Squares beyond ~1.8e19 overflow to +inf: clamping r keeps
-  // every threshold finite (the search then relies on its bounded fallbacks).
-  const float r = fminf(__builtin_amdgcn_sqrtf(s2), 3.0e38f);
+  // the search. Clamping r keeps every threshold finite: the first is at
+  // most ~4r, each Newton step moves by at most (2m + 1) h <= ~50r (h is at
+  // most 1.25r), and there are at most 8 steps, so |t| < 1e38. Rows whose
+  // squares overflow (~1.8e19) get the clamped scale; the search then
+  // relies on its bounded fallbacks.
+  const float r = fminf(__builtin_amdgcn_sqrtf(s2), 1.0e35f);
   const float h = r * a.half_step;
   const float t = r * a.z_first;
   int c;
@@ -612,17 +624,17 @@ __device__ __forceinline__ void exact_row(const float (&vin)[Q],
       float cv[QC];
       int ci[QC];
       read_candidates<Q, QC>(scratch, c, lane, cv, ci);
-      exact_candidates<QC>(cv, ci, k, t, c, h, ov, oi);
+      exact_candidates<QC>(cv, ci, k, t, c, h, out);
       return;
     }
   } else {
     c = count_ge(v, t);
   }
   if (c == k) {
-    emit_ge(v, [lane](int s) { return s * kWave + lane; }, t, ov, oi);
+    emit_ge(v, [lane](int s) { return s * kWave + lane; }, t, out);
     return;
   }
-  exact_row_search<Q, QC, IdxT>(v, k, lane, t, c, h, scratch, ov, oi);
+  exact_row_search<Q, QC, IdxT>(v, k, lane, t, c, h, scratch, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -632,12 +644,11 @@ template <int Q, bool FULL, Mode MODE, int QC, typename IdxT>
 __device__ __forceinline__ void process_row(const float (&v)[Q],
                                             const SelectArgs& a, int lane,
                                             uint32_t* __restrict__ scratch,
-                                            float* __restrict__ ov,
-                                            IdxT* __restrict__ oi) {
+                                            const OutRow<IdxT>& out) {
   if constexpr (MODE == Mode::kExact)
-    exact_row<Q, FULL, QC, IdxT>(v, a, lane, scratch, ov, oi);
+    exact_row<Q, FULL, QC, IdxT>(v, a, lane, scratch, out);
   else
-    capped_row<Q, FULL, IdxT>(v, a, lane, ov, oi);
+    capped_row<Q, FULL, IdxT>(v, a, lane, out);
 }
 
 // Rows each wave keeps in flight: the row being worked on plus D - 1
@@ -704,8 +715,8 @@ __global__ __launch_bounds__(kBlock) void rows_in_registers(SelectArgs a) {
       load_row<Q, FULL>(d + D - 1 < rows_left ? p : xg, a.m, lane,
                         buf[(d + D - 1) % D]);
       if (d >= rows_left) return;
-      process_row<Q, FULL, MODE, QC, IdxT>(buf[d], a, lane, scratch, og + d * k,
-                                           ig + d * k);
+      process_row<Q, FULL, MODE, QC, IdxT>(
+          buf[d], a, lane, scratch, OutRow<IdxT>(og + d * k, ig + d * k, a.k));
     }
     rows_left -= D;
     if (rows_left <= 0) return;
