@@ -206,9 +206,41 @@ def main():
     ms_per_step = total_ms / args.steps
     avg_launch_ms = ms_per_step
 
+    # Spread of single launches (not used for the throughput figure): an event
+    # pair around each of up to 100 further launches.
+    n_single = min(args.steps, 100)
+    pairs = [(torch.cuda.Event(enable_timing=True),
+              torch.cuda.Event(enable_timing=True)) for _ in range(n_single)]
+    for i, (a, b) in enumerate(pairs):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    single_us = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
+
+    def pct(q):
+        return single_us[min(len(single_us) - 1, int(q * len(single_us)))]
+
+    # Practical streaming ceiling of this GPU: an elementwise negation over
+    # 256 MiB (read once, written once), timed the same way.
+    src = torch.ones(COPY_REF_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(20):
+        torch.neg(src, out=dst)
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    c0.record(stream)
+    for _ in range(50):
+        torch.neg(src, out=dst)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * COPY_REF_BYTES / (c0.elapsed_time(c1) / 50 * 1e-3) / 1e9
+    del src, dst
+
     if args.copy_reference:
         # Plain streaming kernel of known size for scaling the HBM counters:
-        # an elementwise negation reads and writes 268,435,456 bytes each.
+        # three more negations, each reading and writing 268,435,456 bytes.
         src = torch.ones(COPY_REF_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
@@ -261,6 +293,9 @@ def main():
                      "traffic": traffic},
         "cpu_baseline": cpu,
         "kernel_avg_us": avg_launch_ms * 1e3,
+        "single_launch_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9),
+                             "launches": n_single},
+        "stream_copy_gbs": copy_gbs,
     }
     print(json.dumps(line), flush=True)
 
