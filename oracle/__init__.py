@@ -11,6 +11,10 @@ survivors per row), ties at the k-th value going to the lowest indices.
 ``capped`` is the threshold search with early stopping and tie fill of the RTop-K
 summary page, "Approach", in the reading spelled out in ``rtopk_oracle.cpp``.
 Both return the survivors of each row in ascending index order.
+``maxk_forward`` / ``maxk_backward`` are the MaxK nonlinearity of the MaxK-GNN
+review ("How MaxK-GNN works"): the dense [N, M] output that keeps each row's
+exact top-k and zeroes the rest, and the gradient that flows back only to the
+survivors' columns.
 """
 
 from __future__ import annotations
@@ -56,6 +60,12 @@ def _load():
                                   ctypes.c_float, ctypes.c_int32, f32p, i32p,
                                   i32p, f32p, f32p]
     lib.oracle_capped.restype = ctypes.c_int
+    lib.oracle_maxk_forward.argtypes = [f32p, ctypes.c_int64, ctypes.c_int32,
+                                        ctypes.c_int32, f32p, f32p, i32p]
+    lib.oracle_maxk_forward.restype = ctypes.c_int
+    lib.oracle_maxk_backward.argtypes = [f32p, i32p, ctypes.c_int64,
+                                         ctypes.c_int32, ctypes.c_int32, f32p]
+    lib.oracle_maxk_backward.restype = ctypes.c_int
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
     _lib = lib
@@ -113,6 +123,33 @@ def capped(x, k: int, max_iter: int = -1, eps: float = 0.0,
     if return_state:
         return vals, idx, counts, lo, hi
     return vals, idx
+
+
+def maxk_forward(x, k: int):
+    """MaxK nonlinearity: (y [N,M], sp_data [N,k], sp_index [N,k] i32)."""
+    x = _as_rows(x)
+    n, m = x.shape
+    y = np.empty((n, m), dtype=np.float32)
+    vals = np.empty((n, k), dtype=np.float32)
+    idx = np.empty((n, k), dtype=np.int32)
+    rc = _load().oracle_maxk_forward(_fp(x), n, m, k, _fp(y), _fp(vals), _ip(idx))
+    if rc != 0:
+        raise ValueError(f"oracle_maxk_forward: invalid arguments (N={n}, M={m}, k={k})")
+    return y, vals, idx
+
+
+def maxk_backward(grad_sp, sp_index, m: int):
+    """Gradient of the MaxK survivors sent back to their columns: [N, m]."""
+    g = np.ascontiguousarray(grad_sp, dtype=np.float32)
+    idx = np.ascontiguousarray(sp_index, dtype=np.int32)
+    if g.ndim != 2 or g.shape != idx.shape:
+        raise ValueError("grad_sp and sp_index must be [N, k] arrays of one shape")
+    n, k = g.shape
+    out = np.empty((n, m), dtype=np.float32)
+    rc = _load().oracle_maxk_backward(_fp(g), _ip(idx), n, m, k, _fp(out))
+    if rc != 0:
+        raise ValueError(f"oracle_maxk_backward: invalid arguments (N={n}, M={m}, k={k})")
+    return out
 
 
 def threads() -> int:

@@ -15,6 +15,15 @@
 //                     survivors are written in ascending index order (the pages
 //                     only ask for unsorted output).
 //
+//   oracle_maxk_forward / oracle_maxk_backward -- the MaxK nonlinearity of
+//                     the MaxK-GNN review ("How MaxK-GNN works"): each row
+//                     keeps its k largest features and the rest become zero;
+//                     the survivors are also given as the compressed pair
+//                     (sp_data, sp_index). Only survivors carry gradient, so
+//                     the backward pass sends the gradient of each survivor
+//                     back to its column through the same sp_index and leaves
+//                     every other column at zero.
+//
 //   oracle_capped  -- the threshold search of the RTop-K summary page, section
 //                     "Approach": bisection over the row's value range until a
 //                     threshold selects k elements, an optional cap on the
@@ -120,7 +129,7 @@ void capped_row(const float* x, int M, int k, int max_iter, float eps,
       hi = mid;
       break;
     }
-    if (c > k)
+    if (c >= k)
       lo = mid;
     else
       hi = mid;
@@ -179,6 +188,53 @@ int oracle_capped(const float* x, int64_t N, int32_t M, int32_t k,
     capped_row(x + r * M, M, k, max_iter, eps, fill_from_row_min,
                out_val + r * k, out_idx + r * k, counts ? counts + r : nullptr,
                lo_out ? lo_out + r : nullptr, hi_out ? hi_out + r : nullptr);
+  }
+  return 0;
+}
+
+// MaxK forward. y is [N, M]: y[r, j] = x[r, j] if column j is one of the
+// row's exact top-k (as oracle_exact chooses them), else +0. sp_data /
+// sp_index ([N, k], optional: pass NULL for both) receive the survivors in
+// ascending column order. Returns 0 on success, 1 on invalid arguments.
+int oracle_maxk_forward(const float* x, int64_t N, int32_t M, int32_t k,
+                        float* y, float* sp_data, int32_t* sp_index) {
+  if (N < 0 || M < 1 || k < 1 || k > M) return 1;
+  if ((sp_data == nullptr) != (sp_index == nullptr)) return 1;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < N; ++r) {
+    std::vector<float> vals(k);
+    std::vector<int32_t> cols(k);
+    exact_row(x + r * M, M, k, vals.data(), cols.data());
+    float* yr = y + r * M;
+    for (int j = 0; j < M; ++j) yr[j] = 0.0f;
+    for (int i = 0; i < k; ++i) yr[cols[i]] = x[r * M + cols[i]];
+    if (sp_data) {
+      for (int i = 0; i < k; ++i) {
+        sp_data[r * k + i] = vals[i];
+        sp_index[r * k + i] = cols[i];
+      }
+    }
+  }
+  return 0;
+}
+
+// MaxK backward: the adjoint of gathering the k survivors of each row.
+// grad_x is [N, M] with grad_x[r, j] = sum over i with sp_index[r, i] == j of
+// grad_sp[r, i] (the sum is taken in double and has at most one term when the
+// row's indices are distinct, as MaxK's are); columns no index names are +0.
+// Indices outside [0, M) contribute nothing. Returns 0, or 1 on invalid
+// arguments.
+int oracle_maxk_backward(const float* grad_sp, const int32_t* sp_index,
+                         int64_t N, int32_t M, int32_t k, float* grad_x) {
+  if (N < 0 || M < 1 || k < 1) return 1;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < N; ++r) {
+    std::vector<double> acc(M, 0.0);
+    for (int i = 0; i < k; ++i) {
+      const int32_t j = sp_index[r * k + i];
+      if (j >= 0 && j < M) acc[j] += static_cast<double>(grad_sp[r * k + i]);
+    }
+    for (int j = 0; j < M; ++j) grad_x[r * M + j] = static_cast<float>(acc[j]);
   }
   return 0;
 }
