@@ -58,9 +58,9 @@ def measured_traffic(workload: str):
     return float(rec["bytes_per_launch"])
 
 
-def _counter_means(csv_path: str, counter: str):
-    """Mean per-dispatch value of one counter for the select kernel and for
-    the negation kernel, from a rocprofv3 counter_collection.csv."""
+def _counter_means(csv_path: str, counter: str, kernel: str):
+    """Mean per-dispatch value of one counter for the op's kernel and for the
+    negation kernel, from a rocprofv3 counter_collection.csv."""
     import csv
     sel, ref = [], []
     with open(csv_path) as f:
@@ -68,7 +68,7 @@ def _counter_means(csv_path: str, counter: str):
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            if "rows_in_registers" in name:
+            if kernel in name:
                 sel.append(float(r["Counter_Value"]))
             elif "neg" in name.lower():
                 ref.append(float(r["Counter_Value"]))
@@ -78,13 +78,13 @@ def _counter_means(csv_path: str, counter: str):
     return sum(sel) / len(sel), sum(ref) / len(ref)
 
 
-def record_traffic(workload: str, fetch_csv: str, write_csv: str) -> None:
+def record_traffic(workload: str, kernel: str, fetch_csv: str, write_csv: str) -> None:
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per
     dispatch) of `bench.py --copy-reference` into HBM bytes per launch. Each
     counter is scaled by the bytes the negation kernel is known to move
     divided by what the same counter reads for it."""
-    f_sel, f_ref = _counter_means(fetch_csv, "FETCH_SIZE")
-    w_sel, w_ref = _counter_means(write_csv, "WRITE_SIZE")
+    f_sel, f_ref = _counter_means(fetch_csv, "FETCH_SIZE", kernel)
+    w_sel, w_ref = _counter_means(write_csv, "WRITE_SIZE", kernel)
     f_scale = COPY_REF_BYTES / (f_ref * 1024.0)
     w_scale = COPY_REF_BYTES / (w_ref * 1024.0)
     fetched = f_sel * 1024.0 * f_scale
@@ -106,14 +106,24 @@ def record_traffic(workload: str, fetch_csv: str, write_csv: str) -> None:
 
 
 def workload_name(args) -> str:
+    if args.op == "maxk_backward":
+        return f"maxk_backward {args.inputs} N={args.rows} M={args.m} k={args.k} idx={args.index}"
     return (f"{args.inputs} N={args.rows} M={args.m} k={args.k} {args.mode}"
             + ("" if args.mode == "exact" else f" max_iter={args.max_iter} eps={args.eps}")
             + f" idx={args.index}")
 
 
+# Name fragment of the kernel each op launches (for the counter records).
+OP_KERNEL = {"select": "rows_in_registers", "maxk_backward": "scatter_rows"}
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--op", choices=["select", "maxk_backward"], default="select",
+                   help="select: row-wise top-k (the headline); maxk_backward: "
+                        "the MaxK gradient scatter on the indices the selection "
+                        "produces for the same rows")
     p.add_argument("--steps", type=int, default=300)
     p.add_argument("--warmup", type=int, default=300,
                    help="untimed launches first; the GPU's clocks take about "
@@ -147,7 +157,7 @@ def main():
               "GPU its own block of rows with no exchange).", file=sys.stderr)
         sys.exit(2)
     if args.record_traffic:
-        record_traffic(workload_name(args), *args.record_traffic)
+        record_traffic(workload_name(args), OP_KERNEL[args.op], *args.record_traffic)
         return
 
     import numpy as np
@@ -176,7 +186,30 @@ def main():
     out_i = torch.empty((n, k), dtype=idx_dtype, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    if args.mode == "exact":
+    if args.op == "maxk_backward":
+        # Inputs: the survivors' indices of each rotated buffer (from the
+        # library's exact selection) and seeded gradients. Outputs rotate too,
+        # so that neither side is served by the last-level cache.
+        sel = rt.rtopk_select_exact_u8 if u8 else rt.rtopk_select_exact
+        rng = np.random.default_rng(7)
+        base_idx = [sel(xb, k)[1] for xb in xs]
+        del xs
+        nbuf = max(1, -(-768 * 2**20 // (n * k * (4 + (1 if u8 else 4)))))
+        grads, idxs = [], []
+        for b in range(nbuf):
+            # Index sets of the selection, rotated by b rows past the first few.
+            ib = base_idx[b % len(base_idx)]
+            idxs.append(ib if b < len(base_idx) else
+                        torch.roll(ib, shifts=b, dims=0).contiguous())
+            grads.append(torch.from_numpy(
+                rng.standard_normal((n, k), dtype=np.float32)).to(dev))
+        nout = max(1, -(-768 * 2**20 // (n * m * 4)))
+        outs = [torch.empty((n, m), dtype=torch.float32, device=dev) for _ in range(nout)]
+
+        def step(i):
+            rt.rtopk_maxk_backward(grads[i % nbuf], idxs[i % nbuf], m,
+                                   grad_x=outs[i % nout])
+    elif args.mode == "exact":
         fn = rt.rtopk_select_exact_u8 if u8 else rt.rtopk_select_exact
 
         def step(i):
@@ -248,7 +281,7 @@ def main():
         torch.cuda.synchronize()
 
     idx_bytes = 1 if u8 else 4
-    per_row = 4 * m + k * (4 + idx_bytes)
+    per_row = 4 * m + k * (4 + idx_bytes)  # same for both ops: M floats one way, k entries the other
     algo_bytes = n * per_row
     achieved = algo_bytes / (avg_launch_ms * 1e-3) / 1e9
     workload = workload_name(args)
@@ -258,10 +291,15 @@ def main():
     if args.cpu_seconds > 0:
         import oracle
         oracle.exact(x_np[:1024], k)  # load and warm
+        if args.op == "maxk_backward":
+            g_np = grads[0].cpu().numpy()
+            i_np = idxs[0].cpu().numpy().astype(np.int32)
         passes, t_cpu = 0, 0.0
         while t_cpu < args.cpu_seconds and passes < 100:
             t = time.perf_counter()
-            if args.mode == "exact":
+            if args.op == "maxk_backward":
+                oracle.maxk_backward(g_np, i_np, m)
+            elif args.mode == "exact":
                 oracle.exact(x_np, k)
             else:
                 oracle.capped(x_np, k, args.max_iter, args.eps)
@@ -273,7 +311,9 @@ def main():
                          f"({t_cpu:.1f} s of oracle time)"}
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC if args.op == "select" else
+                  f"rows/sec and achieved HBM GB/s (% of peak), MaxK backward "
+                  f"N={n} M={m} k={k} fp32",
         "value": n / (ms_per_step * 1e-3),
         "unit": "rows/s",
         "n_gpus": 1,
@@ -285,7 +325,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": workload, "rows": n, "row_length": m, "k": k,
+        "config": {"workload": workload, "op": args.op, "rows": n,
+                   "row_length": m, "k": k,
                    "mode": args.mode, "index": args.index,
                    "input_buffers": nbuf, "bytes_per_row": per_row},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,

@@ -104,6 +104,34 @@ rtopk_status_t rtopk_select_exact_u8(const float* x, int64_t N, int32_t M,
                                      int32_t k, float* out_val,
                                      uint8_t* out_idx, hipStream_t stream);
 
+/*
+ * MaxK backward (MaxK-GNN review, "How MaxK-GNN works": only the survivors of
+ * the MaxK nonlinearity carry gradient, and the backward pass reuses the
+ * sp_index the forward pass produced). Writes the dense [N, M] gradient
+ *   grad_x[r*M + sp_index[r*k + i]] = grad_sp[r*k + i]   for i < k,
+ * and +0.0 in every column no entry of row r names. The same call turns a
+ * compressed row pair (sp_data, sp_index) back into the dense MaxK output.
+ *   grad_sp   device pointer to N*k floats (gradient of the survivors, in
+ *             the order of sp_index), read.
+ *   sp_index  device pointer to N*k int32 column indices, read. The indices
+ *             of a row must be distinct for the result to be defined (MaxK's
+ *             are); with duplicates one of the entries lands, unspecified
+ *             which. Entries outside [0, M) are ignored.
+ *   grad_x    device pointer to N*M floats, written (every element).
+ * N, M, k, stream and the errors are as above (1 <= k <= M <= 8192).
+ * grad_x must not overlap the inputs.
+ */
+rtopk_status_t rtopk_maxk_backward(const float* grad_sp,
+                                   const int32_t* sp_index, int64_t N,
+                                   int32_t M, int32_t k, float* grad_x,
+                                   hipStream_t stream);
+
+/* As rtopk_maxk_backward with one-byte indices. Requires M <= 256. */
+rtopk_status_t rtopk_maxk_backward_u8(const float* grad_sp,
+                                      const uint8_t* sp_index, int64_t N,
+                                      int32_t M, int32_t k, float* grad_x,
+                                      hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* rtopk_status_string(rtopk_status_t status);
 

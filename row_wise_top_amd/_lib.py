@@ -39,8 +39,11 @@ def lib() -> ctypes.CDLL:
     l.rtopk_select_u8.argtypes = [vp, i64, i32, i32, i32, f32, vp, vp, vp]
     l.rtopk_select_exact.argtypes = [vp, i64, i32, i32, vp, vp, vp]
     l.rtopk_select_exact_u8.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+    l.rtopk_maxk_backward.argtypes = [vp, vp, i64, i32, i32, vp, vp]
+    l.rtopk_maxk_backward_u8.argtypes = [vp, vp, i64, i32, i32, vp, vp]
     for f in (l.rtopk_select, l.rtopk_select_u8, l.rtopk_select_exact,
-              l.rtopk_select_exact_u8):
+              l.rtopk_select_exact_u8, l.rtopk_maxk_backward,
+              l.rtopk_maxk_backward_u8):
         f.restype = ctypes.c_int
     l.rtopk_status_string.argtypes = [ctypes.c_int]
     l.rtopk_status_string.restype = ctypes.c_char_p
@@ -128,3 +131,31 @@ def rtopk_select_exact_u8(x, k: int, out_val=None, out_idx=None, stream=None):
                                        out_idx.data_ptr(), _stream(x, stream)),
            "rtopk_select_exact_u8")
     return out_val, out_idx
+
+
+def rtopk_maxk_backward(grad_sp, sp_index, m: int, grad_x=None, stream=None):
+    """Dense [N, m] gradient of the MaxK survivors: grad_x[r, sp_index[r, i]] =
+    grad_sp[r, i], zero elsewhere. sp_index is int32 or uint8 (m <= 256)."""
+    import torch
+    for t in (grad_sp, sp_index):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError("grad_sp and sp_index must be torch tensors on a GPU device")
+    if (grad_sp.dtype != torch.float32 or grad_sp.dim() != 2
+            or not grad_sp.is_contiguous()):
+        raise ValueError("grad_sp must be a contiguous 2-D float32 tensor [N, k]")
+    if (sp_index.dtype not in (torch.int32, torch.uint8) or not sp_index.is_contiguous()
+            or tuple(sp_index.shape) != tuple(grad_sp.shape)
+            or sp_index.device != grad_sp.device):
+        raise ValueError("sp_index must be a contiguous int32 or uint8 tensor shaped like grad_sp")
+    n, k = grad_sp.shape
+    if grad_x is None:
+        grad_x = torch.empty((n, m), dtype=torch.float32, device=grad_sp.device)
+    if (grad_x.device != grad_sp.device or grad_x.dtype != torch.float32
+            or not grad_x.is_contiguous() or tuple(grad_x.shape) != (n, m)):
+        raise ValueError(f"grad_x must be a contiguous [{n}, {m}] float32 tensor on {grad_sp.device}")
+    u8 = sp_index.dtype == torch.uint8
+    fn = lib().rtopk_maxk_backward_u8 if u8 else lib().rtopk_maxk_backward
+    _check(fn(grad_sp.data_ptr(), sp_index.data_ptr(), n, m, k, grad_x.data_ptr(),
+              _stream(grad_sp, stream)),
+           "rtopk_maxk_backward_u8" if u8 else "rtopk_maxk_backward")
+    return grad_x

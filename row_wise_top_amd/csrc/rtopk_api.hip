@@ -35,6 +35,20 @@ rtopk_status_t run(const float* x, int64_t n, int32_t m, int32_t k,
   return err == hipSuccess ? RTOPK_SUCCESS : RTOPK_ERROR_LAUNCH;
 }
 
+rtopk_status_t run_scatter(const float* src, const void* idx, int64_t n,
+                           int32_t m, int32_t k, float* out, bool u8_index,
+                           hipStream_t stream) {
+  if (n < 0 || m < 1 || k < 1 || k > m) return RTOPK_ERROR_INVALID_VALUE;
+  if (m > rtopk::kMaxRowLength) return RTOPK_ERROR_NOT_SUPPORTED;
+  if (u8_index && m > 256) return RTOPK_ERROR_NOT_SUPPORTED;
+  if (n > 0 && (src == nullptr || idx == nullptr || out == nullptr))
+    return RTOPK_ERROR_INVALID_VALUE;
+  if (n == 0) return RTOPK_SUCCESS;
+  const rtopk::ScatterArgs a{src, idx, n, m, k, out};
+  const hipError_t err = rtopk::launch_scatter(a, u8_index, stream);
+  return err == hipSuccess ? RTOPK_SUCCESS : RTOPK_ERROR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -65,6 +79,20 @@ rtopk_status_t rtopk_select_exact_u8(const float* x, int64_t N, int32_t M,
                                      uint8_t* out_idx, hipStream_t stream) {
   return run(x, N, M, k, -1, 0.0f, out_val, out_idx, true,
              rtopk::Mode::kExact, stream);
+}
+
+rtopk_status_t rtopk_maxk_backward(const float* grad_sp,
+                                   const int32_t* sp_index, int64_t N,
+                                   int32_t M, int32_t k, float* grad_x,
+                                   hipStream_t stream) {
+  return run_scatter(grad_sp, sp_index, N, M, k, grad_x, false, stream);
+}
+
+rtopk_status_t rtopk_maxk_backward_u8(const float* grad_sp,
+                                      const uint8_t* sp_index, int64_t N,
+                                      int32_t M, int32_t k, float* grad_x,
+                                      hipStream_t stream) {
+  return run_scatter(grad_sp, sp_index, N, M, k, grad_x, true, stream);
 }
 
 const char* rtopk_status_string(rtopk_status_t status) {

@@ -11,7 +11,6 @@
 #include "rtopk_internal.h"
 
 namespace rtopk {
-namespace {
 
 // Resident blocks per CU for a kernel on a device, cached per device.
 int resident_blocks(const void* fn, int device) {
@@ -45,6 +44,9 @@ int cu_count(int device) {
   }
   return c;
 }
+
+namespace {
+
 
 int slot_bucket(int m) {
   const int slots = (m + kWave - 1) / kWave;

@@ -53,6 +53,27 @@ inline int candidate_slots(int q, int k) {
   return 0;
 }
 
+// Resident blocks per CU of `fn` launched with kBlock threads on `device`,
+// and the device's CU count (both cached per device).
+int resident_blocks(const void* fn, int device);
+int cu_count(int device);
+
+// MaxK backward (and compressed rows to dense): out[r, idx[r, i]] = src[r, i]
+// for every entry with an index in [0, m), every other element of out 0.
+struct ScatterArgs {
+  const float* src;  // [n, k]
+  const void* idx;   // [n, k] int32_t or uint8_t
+  int64_t n;
+  int32_t m;
+  int32_t k;
+  float* out;        // [n, m]
+};
+
+// Enqueue the scatter kernel (rtopk_maxk.hip). Arguments are validated
+// (n > 0, 1 <= k <= m <= kMaxRowLength).
+hipError_t launch_scatter(const ScatterArgs& a, bool u8_index,
+                          hipStream_t stream);
+
 // Enqueue the selection kernel for `a` on `stream`. Arguments are already
 // validated (1 <= k <= m <= kMaxRowLength, n > 0, u8 only with m <= 256).
 // Returns the HIP error of the launch.

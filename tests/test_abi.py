@@ -23,7 +23,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted([
         "rtopk_select", "rtopk_select_exact", "rtopk_select_u8",
-        "rtopk_select_exact_u8", "rtopk_status_string"])
+        "rtopk_select_exact_u8", "rtopk_maxk_backward",
+        "rtopk_maxk_backward_u8", "rtopk_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -97,3 +98,35 @@ def test_null_pointers(fn, which):
     else:
         rc = call(fn, ptrs[0], 4, 16, 4, ptrs[1], ptrs[2], None)
     assert rc == 1
+
+
+BACKWARD = ["rtopk_maxk_backward", "rtopk_maxk_backward_u8"]
+
+
+@pytest.mark.parametrize("fn", BACKWARD)
+def test_backward_n_zero_is_a_noop(fn):
+    assert call(fn, None, None, 0, 16, 4, None, None) == 0
+
+
+@pytest.mark.parametrize("fn", BACKWARD)
+@pytest.mark.parametrize("n,m,k,code", [
+    (-1, 16, 4, 1),      # N < 0
+    (4, 0, 1, 1),        # M < 1
+    (4, 16, 0, 1),       # k < 1
+    (4, 16, 17, 1),      # k > M
+    (4, 8193, 4, 2),     # M above the supported maximum
+])
+def test_backward_shape_errors(fn, n, m, k, code):
+    assert call(fn, FAKE, FAKE, n, m, k, FAKE, None) == code
+
+
+def test_backward_u8_requires_short_rows():
+    assert call("rtopk_maxk_backward_u8", FAKE, FAKE, 4, 257, 4, FAKE, None) == 2
+
+
+@pytest.mark.parametrize("fn", BACKWARD)
+@pytest.mark.parametrize("which", [0, 1, 2])
+def test_backward_null_pointers(fn, which):
+    ptrs = [FAKE, FAKE, FAKE]
+    ptrs[which] = None
+    assert call(fn, ptrs[0], ptrs[1], 4, 16, 4, ptrs[2], None) == 1
