@@ -128,13 +128,21 @@ hipError_t launch_select(const SelectArgs& args, Mode mode, bool u8_index,
   int device = 0;
   hipError_t err = hipGetDevice(&device);
   if (err != hipSuccess) return err;
-  // One wave per row at a time; a persistent grid of what fits on the device
-  // at once (each wave takes rows in groups, so fewer waves may suffice).
-  const int64_t blocks_needed = (a.n + kWavesPerBlock - 1) / kWavesPerBlock;
-  const int64_t resident =
-      static_cast<int64_t>(cu_count(device)) *
-      resident_blocks(reinterpret_cast<const void*>(fn), device);
-  const int64_t grid = blocks_needed < resident ? blocks_needed : resident;
+  // One wave per row at a time, in groups of D = rows_in_flight(q) rows.
+  // Short rows: one group per wave, a grid over the whole matrix (waves exit
+  // after their group). Long rows: a persistent grid of what fits on the
+  // device at once.
+  const int q = slot_bucket(a.m);
+  const int64_t d = rows_in_flight(q);
+  const int64_t per_block = kWavesPerBlock * d;
+  const int64_t blocks_needed = (a.n + per_block - 1) / per_block;
+  int64_t grid = blocks_needed;
+  if (!one_group_per_wave(q) || blocks_needed > 0x7fffffff) {
+    const int64_t resident =
+        static_cast<int64_t>(cu_count(device)) *
+        resident_blocks(reinterpret_cast<const void*>(fn), device);
+    grid = blocks_needed < resident ? blocks_needed : resident;
+  }
   hipLaunchKernelGGL(fn, dim3(static_cast<uint32_t>(grid)), dim3(kBlock), 0,
                      stream, a);
   return hipGetLastError();

@@ -34,6 +34,15 @@ struct SelectArgs {
 
 using RowsKernel = void (*)(SelectArgs);
 
+// Rows a wave of the selection kernel keeps in flight for q slots per lane:
+// the row being worked on plus rows_in_flight(q) - 1 whose loads are
+// issued. Short rows (q <= 16) are also the rows each wave takes in all: the
+// grid then covers the matrix once (a wave that loads its rows first and
+// stores last never waits on its own stores, which share the load counter
+// on this GPU). Longer rows get no prefetch and a persistent grid.
+constexpr int rows_in_flight(int q) { return q <= 4 ? 4 : (q <= 16 ? 2 : 1); }
+constexpr bool one_group_per_wave(int q) { return q <= 16; }
+
 // Slot counts Q (elements per lane) with an instantiated register-resident
 // row kernel; a row of length m uses the smallest Q with 64*Q >= m.
 constexpr int kSlotBuckets[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128};

@@ -20,8 +20,8 @@
 // Compaction in column order needs only the scalar prefix over earlier slots
 // plus the lane's rank inside its slot's mask (mbcnt).
 //
-// Each wave walks rows with a grid stride and issues the loads of its next
-// row before working on the current one, so HBM reads overlap the search.
+// Each wave takes rows in groups and issues the loads of its next rows
+// before working on the current one, so HBM reads overlap the search.
 //
 // Two searches share this skeleton:
 //  * capped (rtopk_select): the bisection of the summary page, step for step
@@ -651,23 +651,23 @@ __device__ __forceinline__ void process_row(const float (&v)[Q],
     capped_row<Q, FULL, IdxT>(v, a, lane, out);
 }
 
-// Rows each wave keeps in flight: the row being worked on plus D - 1
-// prefetched ones. The prefetch loads are unconditional (past the last row
-// they re-read it) so that the compiler's wait counts stay exact and a
-// wave only ever waits for the row it is about to use. Two rows in flight
-// per wave, at the full occupancy the register budget allows for short
-// rows, streamed faster than three rows at fewer waves: more waves hide the
-// search's issue latency, and one extra row per wave already covers the
-// load latency.
+// Rows each wave keeps in flight (rows_in_flight in rtopk_internal.h): the
+// row being worked on plus D - 1 prefetched ones. The prefetch loads are
+// unconditional (past the last row they re-read it) so that the compiler's
+// wait counts stay exact and a wave only ever waits for the row it is about
+// to use. Four rows in flight for rows of at most 256 (measured faster than
+// two or three; 39 VGPRs keep 8 waves per SIMD).
 template <int Q>
 constexpr int prefetch_depth() {
-  return Q <= 16 ? 2 : 1;
+  return rows_in_flight(Q);
 }
 
 // Row order. Wave w of S works through groups of D consecutive rows:
 // group g is rows (g*S + w)*D ... (g*S + w)*D + D - 1. The rows a wave has in
 // flight are neighbours, and at any moment all waves together read one
-// contiguous stretch of the matrix (HBM streams fastest that way).
+// contiguous stretch of the matrix (HBM streams fastest that way). For short
+// rows the host launches enough waves for one group each; the loop below
+// then runs once.
 template <int Q, bool FULL, Mode MODE, int QC, typename IdxT>
 __global__ __launch_bounds__(kBlock) void rows_in_registers(SelectArgs a) {
   // Per wave: the LDS staging area of the exact search, (value, column)
