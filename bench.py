@@ -107,24 +107,27 @@ def record_traffic(workload: str, kernel: str, fetch_csv: str, write_csv: str) -
 
 
 def workload_name(args) -> str:
-    if args.op == "maxk_backward":
-        return f"maxk_backward {args.inputs} N={args.rows} M={args.m} k={args.k} idx={args.index}"
+    if args.op in ("maxk_backward", "maxk_forward"):
+        return f"{args.op} {args.inputs} N={args.rows} M={args.m} k={args.k} idx={args.index}"
     return (f"{args.inputs} N={args.rows} M={args.m} k={args.k} {args.mode}"
             + ("" if args.mode == "exact" else f" max_iter={args.max_iter} eps={args.eps}")
             + f" idx={args.index}")
 
 
 # Name fragment of the kernel each op launches (for the counter records).
-OP_KERNEL = {"select": "rows_in_registers", "maxk_backward": "scatter_rows"}
+OP_KERNEL = {"select": "rows_in_registers", "maxk_forward": "rows_in_registers",
+             "maxk_backward": "scatter_rows"}
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--op", choices=["select", "maxk_backward"], default="select",
-                   help="select: row-wise top-k (the headline); maxk_backward: "
-                        "the MaxK gradient scatter on the indices the selection "
-                        "produces for the same rows")
+    p.add_argument("--op", choices=["select", "maxk_forward", "maxk_backward"],
+                   default="select",
+                   help="select: row-wise top-k (the headline); maxk_forward: "
+                        "the MaxK nonlinearity (dense output plus the compressed "
+                        "pair); maxk_backward: the MaxK gradient scatter on the "
+                        "indices the selection produces for the same rows")
     p.add_argument("--steps", type=int, default=300)
     p.add_argument("--warmup", type=int, default=300,
                    help="untimed launches first; the GPU's clocks take about "
@@ -210,6 +213,13 @@ def main():
         def step(i):
             rt.rtopk_maxk_backward(grads[i % nbuf], idxs[i % nbuf], m,
                                    grad_x=outs[i % nout])
+    elif args.op == "maxk_forward":
+        nout = max(1, -(-768 * 2**20 // (n * m * 4)))
+        ys = [torch.empty((n, m), dtype=torch.float32, device=dev) for _ in range(nout)]
+
+        def step(i):
+            rt.rtopk_maxk_forward(xs[i % nbuf], k, y=ys[i % nout], sp_data=out_v,
+                                  sp_index=out_i, index_dtype=idx_dtype)
     elif args.mode == "exact":
         fn = rt.rtopk_select_exact_u8 if u8 else rt.rtopk_select_exact
 
@@ -282,7 +292,9 @@ def main():
         torch.cuda.synchronize()
 
     idx_bytes = 1 if u8 else 4
-    per_row = 4 * m + k * (4 + idx_bytes)  # same for both ops: M floats one way, k entries the other
+    # select and maxk_backward: M floats one way, k entries the other;
+    # maxk_forward: M floats in, M floats and k entries out.
+    per_row = 4 * m + k * (4 + idx_bytes) + (4 * m if args.op == "maxk_forward" else 0)
     algo_bytes = n * per_row
     achieved = algo_bytes / (avg_launch_ms * 1e-3) / 1e9
     workload = workload_name(args)
@@ -300,6 +312,8 @@ def main():
             t = time.perf_counter()
             if args.op == "maxk_backward":
                 oracle.maxk_backward(g_np, i_np, m)
+            elif args.op == "maxk_forward":
+                oracle.maxk_forward(x_np, k)
             elif args.mode == "exact":
                 oracle.exact(x_np, k)
             else:
@@ -313,8 +327,8 @@ def main():
 
     line = {
         "metric": METRIC if args.op == "select" else
-                  f"rows/sec and achieved HBM GB/s (% of peak), MaxK backward "
-                  f"N={n} M={m} k={k} fp32",
+                  f"rows/sec and achieved HBM GB/s (% of peak), MaxK "
+                  f"{args.op.split('_')[1]} N={n} M={m} k={k} fp32",
         "value": n / (ms_per_step * 1e-3),
         "unit": "rows/s",
         "n_gpus": 1,

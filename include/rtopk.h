@@ -105,6 +105,31 @@ rtopk_status_t rtopk_select_exact_u8(const float* x, int64_t N, int32_t M,
                                      uint8_t* out_idx, hipStream_t stream);
 
 /*
+ * MaxK nonlinearity, forward (MaxK-GNN review, "How MaxK-GNN works": each row
+ * keeps exactly its k largest features and every other feature becomes zero;
+ * the survivors are also kept as the compressed pair sp_data / sp_index that
+ * the aggregation and the backward pass consume). Per row, the survivors are
+ * those of rtopk_select_exact (ties at the k-th value to the lowest columns)
+ * and
+ *   y[r*M + j] = x[r*M + j]   (bit copy) if column j survives, else +0.0,
+ *   sp_data / sp_index        as out_val / out_idx of rtopk_select_exact.
+ *   y         device pointer to N*M floats, written (every element).
+ *   sp_data   device pointer to N*k floats, written.
+ *   sp_index  device pointer to N*k int32 (uint8 for the _u8 form), written.
+ * x, N, M, k, stream and the errors are as above. Rows of at most 1024
+ * elements take one kernel; longer rows take two, enqueued on `stream` in
+ * order. y must not overlap x or the other outputs.
+ */
+rtopk_status_t rtopk_maxk_forward(const float* x, int64_t N, int32_t M,
+                                  int32_t k, float* y, float* sp_data,
+                                  int32_t* sp_index, hipStream_t stream);
+
+/* As rtopk_maxk_forward with one-byte indices. Requires M <= 256. */
+rtopk_status_t rtopk_maxk_forward_u8(const float* x, int64_t N, int32_t M,
+                                     int32_t k, float* y, float* sp_data,
+                                     uint8_t* sp_index, hipStream_t stream);
+
+/*
  * MaxK backward (MaxK-GNN review, "How MaxK-GNN works": only the survivors of
  * the MaxK nonlinearity carry gradient, and the backward pass reuses the
  * sp_index the forward pass produced). Writes the dense [N, M] gradient

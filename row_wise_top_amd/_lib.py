@@ -39,10 +39,13 @@ def lib() -> ctypes.CDLL:
     l.rtopk_select_u8.argtypes = [vp, i64, i32, i32, i32, f32, vp, vp, vp]
     l.rtopk_select_exact.argtypes = [vp, i64, i32, i32, vp, vp, vp]
     l.rtopk_select_exact_u8.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+    l.rtopk_maxk_forward.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
+    l.rtopk_maxk_forward_u8.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
     l.rtopk_maxk_backward.argtypes = [vp, vp, i64, i32, i32, vp, vp]
     l.rtopk_maxk_backward_u8.argtypes = [vp, vp, i64, i32, i32, vp, vp]
     for f in (l.rtopk_select, l.rtopk_select_u8, l.rtopk_select_exact,
-              l.rtopk_select_exact_u8, l.rtopk_maxk_backward,
+              l.rtopk_select_exact_u8, l.rtopk_maxk_forward,
+              l.rtopk_maxk_forward_u8, l.rtopk_maxk_backward,
               l.rtopk_maxk_backward_u8):
         f.restype = ctypes.c_int
     l.rtopk_status_string.argtypes = [ctypes.c_int]
@@ -131,6 +134,29 @@ def rtopk_select_exact_u8(x, k: int, out_val=None, out_idx=None, stream=None):
                                        out_idx.data_ptr(), _stream(x, stream)),
            "rtopk_select_exact_u8")
     return out_val, out_idx
+
+
+def rtopk_maxk_forward(x, k: int, y=None, sp_data=None, sp_index=None,
+                       index_dtype=None, stream=None):
+    """MaxK nonlinearity: (y [N, M] with each row's exact top-k kept and the
+    rest zero, sp_data [N, k], sp_index [N, k]). index_dtype: torch.int32
+    (default) or torch.uint8 (M <= 256)."""
+    import torch
+    idx_dtype = torch.int32 if index_dtype is None else index_dtype
+    if idx_dtype not in (torch.int32, torch.uint8):
+        raise ValueError("index_dtype must be torch.int32 or torch.uint8")
+    n, m, sp_data, sp_index = _prepare(x, k, sp_data, sp_index, idx_dtype)
+    if y is None:
+        y = torch.empty((n, m), dtype=torch.float32, device=x.device)
+    if (y.device != x.device or y.dtype != torch.float32 or not y.is_contiguous()
+            or tuple(y.shape) != (n, m)):
+        raise ValueError(f"y must be a contiguous [{n}, {m}] float32 tensor on {x.device}")
+    u8 = idx_dtype == torch.uint8
+    fn = lib().rtopk_maxk_forward_u8 if u8 else lib().rtopk_maxk_forward
+    _check(fn(x.data_ptr(), n, m, k, y.data_ptr(), sp_data.data_ptr(),
+              sp_index.data_ptr(), _stream(x, stream)),
+           "rtopk_maxk_forward_u8" if u8 else "rtopk_maxk_forward")
+    return y, sp_data, sp_index
 
 
 def rtopk_maxk_backward(grad_sp, sp_index, m: int, grad_x=None, stream=None):

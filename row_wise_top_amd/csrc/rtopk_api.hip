@@ -30,7 +30,7 @@ rtopk_status_t run(const float* x, int64_t n, int32_t m, int32_t k,
       validate(x, n, m, k, eps, out_val, out_idx, u8_index);
   if (st != RTOPK_SUCCESS) return st;
   if (n == 0) return RTOPK_SUCCESS;
-  rtopk::SelectArgs a{x, n, m, k, max_iter, eps, out_val, out_idx, 0.0f, 0.0f};
+  rtopk::SelectArgs a{x, n, m, k, max_iter, eps, out_val, out_idx, 0.0f, 0.0f, nullptr};
   const hipError_t err = rtopk::launch_select(a, mode, u8_index, stream);
   return err == hipSuccess ? RTOPK_SUCCESS : RTOPK_ERROR_LAUNCH;
 }
@@ -46,6 +46,33 @@ rtopk_status_t run_scatter(const float* src, const void* idx, int64_t n,
   if (n == 0) return RTOPK_SUCCESS;
   const rtopk::ScatterArgs a{src, idx, n, m, k, out};
   const hipError_t err = rtopk::launch_scatter(a, u8_index, stream);
+  return err == hipSuccess ? RTOPK_SUCCESS : RTOPK_ERROR_LAUNCH;
+}
+
+// MaxK forward: the exact selection with the dense output. Rows the fused
+// kernel takes in one launch; longer rows run the selection into (sp_data,
+// sp_index) and then scatter those into y, on the same stream.
+rtopk_status_t run_maxk_forward(const float* x, int64_t n, int32_t m, int32_t k,
+                                float* y, float* sp_data, void* sp_index,
+                                bool u8_index, hipStream_t stream) {
+  const rtopk_status_t st =
+      validate(x, n, m, k, 0.0f, sp_data, sp_index, u8_index);
+  if (st != RTOPK_SUCCESS) return st;
+  if (n > 0 && y == nullptr) return RTOPK_ERROR_INVALID_VALUE;
+  if (n == 0) return RTOPK_SUCCESS;
+  const int q = (m + rtopk::kWave - 1) / rtopk::kWave;
+  rtopk::SelectArgs a{x, n, m, k, -1, 0.0f, sp_data, sp_index, 0.0f, 0.0f, y};
+  hipError_t err;
+  if (rtopk::maxk_fused(q)) {
+    err = rtopk::launch_select(a, rtopk::Mode::kMaxk, u8_index, stream);
+  } else {
+    a.dense = nullptr;
+    err = rtopk::launch_select(a, rtopk::Mode::kExact, u8_index, stream);
+    if (err == hipSuccess) {
+      const rtopk::ScatterArgs s{sp_data, sp_index, n, m, k, y};
+      err = rtopk::launch_scatter(s, u8_index, stream);
+    }
+  }
   return err == hipSuccess ? RTOPK_SUCCESS : RTOPK_ERROR_LAUNCH;
 }
 
@@ -79,6 +106,18 @@ rtopk_status_t rtopk_select_exact_u8(const float* x, int64_t N, int32_t M,
                                      uint8_t* out_idx, hipStream_t stream) {
   return run(x, N, M, k, -1, 0.0f, out_val, out_idx, true,
              rtopk::Mode::kExact, stream);
+}
+
+rtopk_status_t rtopk_maxk_forward(const float* x, int64_t N, int32_t M,
+                                  int32_t k, float* y, float* sp_data,
+                                  int32_t* sp_index, hipStream_t stream) {
+  return run_maxk_forward(x, N, M, k, y, sp_data, sp_index, false, stream);
+}
+
+rtopk_status_t rtopk_maxk_forward_u8(const float* x, int64_t N, int32_t M,
+                                     int32_t k, float* y, float* sp_data,
+                                     uint8_t* sp_index, hipStream_t stream) {
+  return run_maxk_forward(x, N, M, k, y, sp_data, sp_index, true, stream);
 }
 
 rtopk_status_t rtopk_maxk_backward(const float* grad_sp,

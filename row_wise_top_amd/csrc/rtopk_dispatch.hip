@@ -119,7 +119,7 @@ hipError_t launch_select(const SelectArgs& args, Mode mode, bool u8_index,
                          hipStream_t stream) {
   SelectArgs a = args;
   int qc = 0;
-  if (mode == Mode::kExact) {
+  if (mode != Mode::kCapped) {
     qc = candidate_slots(slot_bucket(a.m), a.k);
     exact_model(a, qc);
   }

@@ -14,7 +14,8 @@ constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = kWave * kWavesPerBlock;
 
-enum class Mode { kCapped, kExact };
+// kMaxk: the exact search, plus the dense [n, m] MaxK output (SelectArgs::dense).
+enum class Mode { kCapped, kExact, kMaxk };
 
 struct SelectArgs {
   const float* x;
@@ -30,6 +31,7 @@ struct SelectArgs {
   // With r = sqrt(sum of squares of the row) = rms * sqrt(m):
   float z_first;     // first threshold = r * z_first
   float half_step;   // Newton step per doubled count = r * half_step
+  float* dense;      // Mode::kMaxk only: [n, m] output, survivors kept, rest 0
 };
 
 using RowsKernel = void (*)(SelectArgs);
@@ -42,6 +44,10 @@ using RowsKernel = void (*)(SelectArgs);
 // on this GPU). Longer rows get no prefetch and a persistent grid.
 constexpr int rows_in_flight(int q) { return q <= 4 ? 4 : (q <= 16 ? 2 : 1); }
 constexpr bool one_group_per_wave(int q) { return q <= 16; }
+
+// Rows the fused MaxK forward kernel takes (its LDS holds the dense row);
+// longer rows run the selection and then the scatter.
+constexpr bool maxk_fused(int q) { return q <= 16; }
 
 // Slot counts Q (elements per lane) with an instantiated register-resident
 // row kernel; a row of length m uses the smallest Q with 64*Q >= m.

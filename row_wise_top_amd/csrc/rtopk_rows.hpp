@@ -216,18 +216,31 @@ constexpr int kRsrcWord3 = 0x00020000;
 // four still a valid 32-bit offset.
 constexpr uint32_t kDropPos = 1u << 28;
 
-template <typename IdxT>
+// DENSE (MaxK forward): every survivor is also written, as value bits, to
+// its column of the wave's LDS copy of the dense row (zeroed before the row
+// and stored after it); lanes not selected write their spare word instead.
+template <typename IdxT, bool DENSE>
 struct OutRow {
   __amdgpu_buffer_rsrc_t val;
   __amdgpu_buffer_rsrc_t idx;
+  uint32_t* dense;  // DENSE only: the LDS row (plus one spare word per lane)
+  uint32_t spare;   // DENSE only: this lane's spare word
 
-  __device__ __forceinline__ OutRow(float* ov, IdxT* oi, int k)
+  __device__ __forceinline__ OutRow(float* ov, IdxT* oi, int k,
+                                    uint32_t* dense_row, uint32_t spare_word)
       : val(__builtin_amdgcn_make_buffer_rsrc(ov, 0, k * 4, kRsrcWord3)),
         idx(__builtin_amdgcn_make_buffer_rsrc(
-            oi, 0, k * static_cast<int>(sizeof(IdxT)), kRsrcWord3)) {}
+            oi, 0, k * static_cast<int>(sizeof(IdxT)), kRsrcWord3)),
+        dense(dense_row),
+        spare(spare_word) {}
 
-  // Entry `pos` of the row gets (x, col); pos == kDropPos stores nothing.
-  __device__ __forceinline__ void put(uint32_t pos, float x, int col) const {
+  // Lanes whose bit of `msk` is set emit (x, col) as entry `rank` of the row;
+  // the others store nothing.
+  __device__ __forceinline__ void put(uint64_t msk, uint32_t rank, float x,
+                                      int col) const {
+    const uint32_t pos = lane_select(msk, rank, kDropPos);
+    if constexpr (DENSE)
+      dense[lane_select(msk, static_cast<uint32_t>(col), spare)] = __float_as_uint(x);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), val,
                                           static_cast<int>(pos * 4u), 0, 0);
     if constexpr (sizeof(IdxT) == 1) {
@@ -242,10 +255,10 @@ struct OutRow {
 
 // The second pass: the first k (by column) of A = {x >= hi}, then of
 // B = {lo <= x < hi}. Requires #{x >= lo} >= k.
-template <int S, typename IdxT, typename ColFn>
+template <int S, typename Out, typename ColFn>
 __device__ __forceinline__ void emit_fill(const float (&v)[S], ColFn col,
                                           float lo, float hi, int k,
-                                          const OutRow<IdxT>& out) {
+                                          const Out& out) {
   int nA = 0;
 #pragma unroll
   for (int s = 0; s < S; ++s) nA += popc(ballot(v[s] >= hi));
@@ -278,7 +291,7 @@ __device__ __forceinline__ void emit_fill(const float (&v)[S], ColFn col,
       accB += pb;
     }
     const uint64_t mS = ballot(selA || selB);
-    out.put(lane_select(mS, rank_below(mS, base), kDropPos), v[s], col(s));
+    out.put(mS, rank_below(mS, base), v[s], col(s));
     base += popc(mS);
   }
 }
@@ -287,10 +300,10 @@ __device__ __forceinline__ void emit_fill(const float (&v)[S], ColFn col,
 // Capped search (rtopk_select): the specification in rtopk.h, step for step.
 // Invariant: #{x >= lo} >= k and (#{x >= hi} < k or hi == row max).
 // ---------------------------------------------------------------------------
-template <int Q, bool FULL, typename IdxT>
+template <int Q, bool FULL, typename Out>
 __device__ __forceinline__ void capped_row(const float (&vin)[Q],
                                            const SelectArgs& a, int lane,
-                                           const OutRow<IdxT>& out) {
+                                           const Out& out) {
   float v[Q];
   float mn = kInf, mx = -kInf;
 #pragma unroll
@@ -367,24 +380,24 @@ __device__ __forceinline__ float next_float(float f) {
 
 // Every element >= t (the caller has counted exactly k), in column order.
 // The lane masks come straight from the compares and select the positions.
-template <int S, typename IdxT, typename ColFn>
+template <int S, typename Out, typename ColFn>
 __device__ __forceinline__ void emit_ge(const float (&v)[S], ColFn col,
-                                        float t, const OutRow<IdxT>& out) {
+                                        float t, const Out& out) {
   uint32_t base = 0;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const uint64_t msk = ballot(v[s] >= t);
-    out.put(lane_select(msk, rank_below(msk, base), kDropPos), v[s], col(s));
+    out.put(msk, rank_below(msk, base), v[s], col(s));
     base += popc(msk);
   }
 }
 
 // Order-key bisection until a count equals k or lo, hi are adjacent floats
 // (at most 32 counts), then the emission.
-template <int S, typename IdxT, typename ColFn>
+template <int S, typename Out, typename ColFn>
 __device__ __forceinline__ void finish_by_keys(const float (&v)[S], ColFn col,
                                                int k, float lo, float hi,
-                                               const OutRow<IdxT>& out) {
+                                               const Out& out) {
   int32_t klo = order_key(lo);
   int32_t khi = order_key(hi);
 #pragma unroll 1
@@ -411,11 +424,11 @@ __device__ __forceinline__ void finish_by_keys(const float (&v)[S], ColFn col,
 // u = largest candidate below hi is the k-th largest iff #{x >= u} >= k;
 // from below, u = smallest candidate >= lo is iff #{x > u} <= k. The side
 // with fewer values to settle is taken.
-template <int QC, typename IdxT, typename ColFn>
+template <int QC, typename Out, typename ColFn>
 __device__ __forceinline__ void settle_candidates(const float (&cv)[QC],
                                                   ColFn col, int k, float lo,
                                                   int clo, float hi, int chi,
-                                                  const OutRow<IdxT>& out) {
+                                                  const Out& out) {
 #pragma unroll 1
   for (int it = 0; it < kCandSnaps; ++it) {
     const int need = k - chi;           // survivors still to take from [lo, hi)
@@ -456,11 +469,11 @@ __device__ __forceinline__ void settle_candidates(const float (&cv)[QC],
 // through; a count of exactly k ends the row right there (the emission uses
 // the compares of that count). Otherwise the row is settled from the bracket
 // given by the start and the last step.
-template <int QC, typename IdxT>
+template <int QC, typename Out>
 __device__ __forceinline__ void exact_candidates(const float (&cv)[QC],
                                                  const int (&ci)[QC], int k,
                                                  float t0, int c0, float h,
-                                                 const OutRow<IdxT>& out) {
+                                                 const Out& out) {
   auto col = [&ci](int s) { return ci[s]; };
   // t + (2c - target2) h, as an fma on the count (vector arithmetic only).
   const float h2 = 2.0f * h;
@@ -549,12 +562,12 @@ __device__ __forceinline__ void read_candidates(const uint32_t* __restrict__ scr
 // Full-row search when the first count missed the candidate window: Newton
 // steps on the whole row (compacting as soon as a count lands in (k, W]),
 // then order-key bisection.
-template <int Q, int QC, typename IdxT>
+template <int Q, int QC, typename Out>
 __device__ __forceinline__ void exact_row_search(const float (&v)[Q], int k,
                                               int lane, float t, int c,
                                               float h,
                                               uint32_t* __restrict__ scratch,
-                                              const OutRow<IdxT>& out) {
+                                              const Out& out) {
   constexpr int kW = kWave * QC;
   const int target2 = QC > 0 ? k + kW : 2 * k + 1;
   const float h2 = 2.0f * h;
@@ -587,11 +600,11 @@ __device__ __forceinline__ void exact_row_search(const float (&v)[Q], int k,
   finish_by_keys(v, col, k, lo, hi, out);
 }
 
-template <int Q, bool FULL, int QC, typename IdxT>
+template <int Q, bool FULL, int QC, typename Out>
 __device__ __forceinline__ void exact_row(const float (&vin)[Q],
                                           const SelectArgs& a, int lane,
                                           uint32_t* __restrict__ scratch,
-                                          const OutRow<IdxT>& out) {
+                                          const Out& out) {
   const int k = a.k;
   float v[Q];
   // Scale of the row for the model behind the thresholds (the model assumes
@@ -634,21 +647,21 @@ __device__ __forceinline__ void exact_row(const float (&vin)[Q],
     emit_ge(v, [lane](int s) { return s * kWave + lane; }, t, out);
     return;
   }
-  exact_row_search<Q, QC, IdxT>(v, k, lane, t, c, h, scratch, out);
+  exact_row_search<Q, QC>(v, k, lane, t, c, h, scratch, out);
 }
 
 // ---------------------------------------------------------------------------
 // The kernel: persistent waves, one row at a time, next rows prefetched.
 // ---------------------------------------------------------------------------
-template <int Q, bool FULL, Mode MODE, int QC, typename IdxT>
+template <int Q, bool FULL, Mode MODE, int QC, typename Out>
 __device__ __forceinline__ void process_row(const float (&v)[Q],
                                             const SelectArgs& a, int lane,
                                             uint32_t* __restrict__ scratch,
-                                            const OutRow<IdxT>& out) {
-  if constexpr (MODE == Mode::kExact)
-    exact_row<Q, FULL, QC, IdxT>(v, a, lane, scratch, out);
+                                            const Out& out) {
+  if constexpr (MODE != Mode::kCapped)
+    exact_row<Q, FULL, QC>(v, a, lane, scratch, out);
   else
-    capped_row<Q, FULL, IdxT>(v, a, lane, out);
+    capped_row<Q, FULL>(v, a, lane, out);
 }
 
 // Rows each wave keeps in flight (rows_in_flight in rtopk_internal.h): the
@@ -672,13 +685,20 @@ template <int Q, bool FULL, Mode MODE, int QC, typename IdxT>
 __global__ __launch_bounds__(kBlock) void rows_in_registers(SelectArgs a) {
   // Per wave: the LDS staging area of the exact search, (value, column)
   // pairs (see stage_entries).
-  constexpr int kScratch = (MODE == Mode::kExact && QC > 0) ? 2 * stage_entries<Q, QC>() : 1;
+  constexpr int kScratch = (MODE != Mode::kCapped && QC > 0) ? 2 * stage_entries<Q, QC>() : 1;
   constexpr int D = prefetch_depth<Q>();
+  // MaxK forward: the wave's LDS copy of the dense row (64*Q words) and one
+  // spare word per lane.
+  constexpr bool kDense = MODE == Mode::kMaxk;
+  constexpr int kDenseWords = kDense ? kWave * (Q + 1) : 1;
   __shared__ uint32_t scratch_all[kWavesPerBlock][kScratch];
+  __shared__ uint32_t dense_all[kWavesPerBlock][kDenseWords];
   const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
   const int wave_in_block =
       __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   uint32_t* scratch = scratch_all[wave_in_block];
+  uint32_t* dense = dense_all[wave_in_block];
+  const uint32_t spare = static_cast<uint32_t>(kWave * Q + lane);
   const int64_t waves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
   const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_in_block;
   int64_t r = w * D;  // first row of the current group
@@ -699,6 +719,7 @@ __global__ __launch_bounds__(kBlock) void rows_in_registers(SelectArgs a) {
   const float* xg = a.x + r * m;  // current group
   float* og = a.out_val + r * k;
   IdxT* ig = static_cast<IdxT*>(a.out_idx) + r * k;
+  float* yg = kDense ? a.dense + r * m : nullptr;
   float buf[D][Q];
   // Unconditional loads (rows past this wave's last one re-read its last
   // row) so that the compiler's wait counts need no worst-case assumption.
@@ -715,14 +736,34 @@ __global__ __launch_bounds__(kBlock) void rows_in_registers(SelectArgs a) {
       load_row<Q, FULL>(d + D - 1 < rows_left ? p : xg, a.m, lane,
                         buf[(d + D - 1) % D]);
       if (d >= rows_left) return;
-      process_row<Q, FULL, MODE, QC, IdxT>(
-          buf[d], a, lane, scratch, OutRow<IdxT>(og + d * k, ig + d * k, a.k));
+      if constexpr (kDense) {
+#pragma unroll
+        for (int s = 0; s < Q; ++s) dense[s * kWave + lane] = 0u;
+        // LDS operations of one wave complete in issue order; the barriers
+        // keep the compiler from moving them across each other.
+        __builtin_amdgcn_wave_barrier();
+      }
+      process_row<Q, FULL, MODE, QC>(
+          buf[d], a, lane, scratch,
+          OutRow<IdxT, kDense>(og + d * k, ig + d * k, a.k, dense, spare));
+      if constexpr (kDense) {
+        __builtin_amdgcn_wave_barrier();
+        // The dense row, stores past its end dropped.
+        const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+            yg + d * m, 0, a.m * 4, kRsrcWord3);
+#pragma unroll
+        for (int s = 0; s < Q; ++s)
+          __builtin_amdgcn_raw_buffer_store_b32(dense[s * kWave + lane], ry,
+                                                (s * kWave + lane) * 4, 0, 0);
+        __builtin_amdgcn_wave_barrier();
+      }
     }
     rows_left -= D;
     if (rows_left <= 0) return;
     xg += group_rows * m;
     og += group_rows * k;
     ig += group_rows * k;
+    if constexpr (kDense) yg += group_rows * m;
   }
 }
 
@@ -732,34 +773,38 @@ constexpr bool exact_qc_built(int q, int qc) {
   return qc == 0 || ((qc == 1 || qc == 2 || qc == 4 || qc == 8) && 2 * qc <= q);
 }
 
-template <int Q, bool FULL, typename IdxT>
+template <int Q, bool FULL, Mode MODE, typename IdxT>
 RowsKernel exact_kernel(int qc) {
   switch (qc) {
     case 1:
       if constexpr (exact_qc_built(Q, 1))
-        return rows_in_registers<Q, FULL, Mode::kExact, 1, IdxT>;
+        return rows_in_registers<Q, FULL, MODE, 1, IdxT>;
       break;
     case 2:
       if constexpr (exact_qc_built(Q, 2))
-        return rows_in_registers<Q, FULL, Mode::kExact, 2, IdxT>;
+        return rows_in_registers<Q, FULL, MODE, 2, IdxT>;
       break;
     case 4:
       if constexpr (exact_qc_built(Q, 4))
-        return rows_in_registers<Q, FULL, Mode::kExact, 4, IdxT>;
+        return rows_in_registers<Q, FULL, MODE, 4, IdxT>;
       break;
     case 8:
       if constexpr (exact_qc_built(Q, 8))
-        return rows_in_registers<Q, FULL, Mode::kExact, 8, IdxT>;
+        return rows_in_registers<Q, FULL, MODE, 8, IdxT>;
       break;
     default:
       break;
   }
-  return rows_in_registers<Q, FULL, Mode::kExact, 0, IdxT>;
+  return rows_in_registers<Q, FULL, MODE, 0, IdxT>;
 }
 
 template <int Q, bool FULL, typename IdxT>
 RowsKernel any_kernel(Mode mode, int qc) {
-  if (mode == Mode::kExact) return exact_kernel<Q, FULL, IdxT>(qc);
+  if (mode == Mode::kExact) return exact_kernel<Q, FULL, Mode::kExact, IdxT>(qc);
+  if (mode == Mode::kMaxk) {
+    if constexpr (maxk_fused(Q)) return exact_kernel<Q, FULL, Mode::kMaxk, IdxT>(qc);
+    return nullptr;
+  }
   return rows_in_registers<Q, FULL, Mode::kCapped, 0, IdxT>;
 }
 
@@ -768,7 +813,8 @@ RowsKernel any_kernel(Mode mode, int qc) {
 // The row kernel for Q slots per lane (row length up to 64*Q), one of the
 // buckets listed in rtopk_internal.h. full: the row length is exactly 64*Q
 // (only distinguished for Q <= 4). qc: candidate slots for the exact search
-// (see candidate_slots). Returns nullptr for one-byte indices with Q > 4.
+// (see candidate_slots). Returns nullptr for one-byte indices with Q > 4,
+// and for Mode::kMaxk with rows too long for the fused kernel.
 template <int Q>
 RowsKernel rows_kernel(bool full, Mode mode, bool u8_index, int qc) {
   using rows_detail::any_kernel;

@@ -23,8 +23,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted([
         "rtopk_select", "rtopk_select_exact", "rtopk_select_u8",
-        "rtopk_select_exact_u8", "rtopk_maxk_backward",
-        "rtopk_maxk_backward_u8", "rtopk_status_string"])
+        "rtopk_select_exact_u8", "rtopk_maxk_forward", "rtopk_maxk_forward_u8",
+        "rtopk_maxk_backward", "rtopk_maxk_backward_u8", "rtopk_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -130,3 +130,31 @@ def test_backward_null_pointers(fn, which):
     ptrs = [FAKE, FAKE, FAKE]
     ptrs[which] = None
     assert call(fn, ptrs[0], ptrs[1], 4, 16, 4, ptrs[2], None) == 1
+
+
+FORWARD = ["rtopk_maxk_forward", "rtopk_maxk_forward_u8"]
+
+
+@pytest.mark.parametrize("fn", FORWARD)
+def test_forward_n_zero_is_a_noop(fn):
+    assert call(fn, None, 0, 16, 4, None, None, None, None) == 0
+
+
+@pytest.mark.parametrize("fn", FORWARD)
+@pytest.mark.parametrize("n,m,k,code", [
+    (-1, 16, 4, 1), (4, 0, 1, 1), (4, 16, 0, 1), (4, 16, 17, 1), (4, 8193, 4, 2),
+])
+def test_forward_shape_errors(fn, n, m, k, code):
+    assert call(fn, FAKE, n, m, k, FAKE, FAKE, FAKE, None) == code
+
+
+def test_forward_u8_requires_short_rows():
+    assert call("rtopk_maxk_forward_u8", FAKE, 4, 257, 4, FAKE, FAKE, FAKE, None) == 2
+
+
+@pytest.mark.parametrize("fn", FORWARD)
+@pytest.mark.parametrize("which", [0, 1, 2, 3])
+def test_forward_null_pointers(fn, which):
+    ptrs = [FAKE, FAKE, FAKE, FAKE]
+    ptrs[which] = None
+    assert call(fn, ptrs[0], 4, 16, 4, ptrs[1], ptrs[2], ptrs[3], None) == 1

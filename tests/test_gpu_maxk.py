@@ -1,15 +1,18 @@
-"""GPU parity of the MaxK backward (rtopk_maxk_backward[_u8]) against the
-oracle, bit for bit.
+"""GPU parity of the MaxK nonlinearity against the oracle, bit for bit:
+the backward scatter (rtopk_maxk_backward[_u8]) and the forward
+(rtopk_maxk_forward[_u8]: dense output plus the compressed pair).
 
-The scatter does no arithmetic: every output element is either the bits of
-one input entry or +0.0, so the bar is identity with oracle.maxk_backward on
-rows whose indices are distinct. Index sets come from the oracle's exact top-k
-of seeded workload rows (ascending, as the forward pass produces them) and
-from seeded random permutations (unsorted), with out-of-range entries mixed
-in where the index type allows them. Shapes cover both kernels (one LDS pass
-for M <= 1024 and k <= 256, chunked passes otherwise), 16-byte and 4-byte
-stores (M % 4, a misaligned output), ragged row counts and the full
-262,144 x 256 headline shape.
+Neither does arithmetic on the values it moves: every dense element is the
+bits of one input element or +0.0, so the bar is identity with
+oracle.maxk_backward (on rows whose indices are distinct) and with
+oracle.maxk_forward. Backward index sets come from the oracle's exact top-k of
+seeded workload rows (ascending, as the forward pass produces them) and from
+seeded random permutations (unsorted), with out-of-range entries mixed in
+where the index type allows them. Shapes cover every kernel path (the
+one-pass and chunked scatters, the fused forward up to 1024 columns and the
+two-launch forward beyond), 16-byte and 4-byte stores (M % 4, misaligned
+outputs), adversarial rows (ties, +-0, subnormals, +-FLT_MAX), ragged row
+counts and the full 262,144 x 256 headline shape.
 """
 
 import numpy as np
@@ -143,3 +146,84 @@ def test_full_headline_shape():
     g = rng.standard_normal((n, k)).astype(np.float32)
     assert_bits_equal(gpu_backward(g, idx, m, u8=True), oracle.maxk_backward(g, idx, m),
                       "262144 x 256 u8")
+
+
+# --------------------------------------------------------------------------
+# MaxK forward (rtopk_maxk_forward[_u8]): dense output plus compressed pair.
+# --------------------------------------------------------------------------
+
+def gpu_forward(x_np, k, u8=False, y=None):
+    x = torch.from_numpy(np.ascontiguousarray(x_np)).to(dev())
+    yy, v, i = rt().rtopk_maxk_forward(x, k, y=y, index_dtype=torch.uint8 if u8 else None)
+    torch.cuda.synchronize()
+    return yy.cpu().numpy(), v.cpu().numpy(), i.cpu().numpy().astype(np.int32)
+
+
+def assert_forward_equal(got, want, label):
+    gy, gv, gi = got
+    wy, wv, wi = want
+    assert_bits_equal(gy, wy, label + " y")
+    assert_bits_equal(gv, wv, label + " sp_data")
+    bad = np.flatnonzero((gi != wi).any(axis=1))
+    assert bad.size == 0, f"{label} sp_index: {bad.size} rows differ, first {bad[0]}"
+
+
+FORWARD_SHAPES = [  # (n, m, k): every slot bucket; fused up to 1024, two launches beyond
+    (5, 1, 1), (33, 5, 2), (64, 63, 7), (100, 64, 32), (129, 100, 10), (77, 200, 64),
+    (300, 255, 32), (1000, 256, 32), (70, 256, 256), (257, 257, 32), (60, 300, 150),
+    (50, 500, 16), (40, 512, 100), (30, 700, 64), (20, 1000, 500), (65, 1024, 64),
+    (20, 1025, 32), (16, 2048, 64), (8, 5000, 2500), (6, 8192, 256),
+]
+
+
+@pytest.mark.parametrize("n,m,k", FORWARD_SHAPES)
+@pytest.mark.parametrize("data", ["normal", "maxk", "grid"])
+def test_forward_shapes(n, m, k, data):
+    if data == "normal":
+        x = workloads.normal(n, m, 300 + m)
+    elif data == "maxk":
+        x = workloads.maxk_activation(n, m, workloads.CONFIG_SEEDS[3])
+    else:
+        x = workloads.grid_ties(n, m, 5)
+    want = oracle.maxk_forward(x, k)
+    assert_forward_equal(gpu_forward(x, k), want, f"i32 {data} n={n} m={m} k={k}")
+    if m <= 256:
+        assert_forward_equal(gpu_forward(x, k, u8=True), want, f"u8 {data} n={n} m={m} k={k}")
+
+
+@pytest.mark.parametrize("m", [1, 3, 64, 100, 256, 1000, 1024, 2000])
+def test_forward_adversarial_rows(m):
+    x = workloads.adversarial_rows(m)
+    for k in sorted({1, max(1, m // 3), max(1, m - 1), m}):
+        assert_forward_equal(gpu_forward(x, k), oracle.maxk_forward(x, k),
+                             f"adversarial m={m} k={k}")
+
+
+@pytest.mark.parametrize("m", [256, 2048])
+def test_forward_misaligned_dense_output(m):
+    n, k = 150, 32
+    x = workloads.normal(n, m, 400 + m)
+    guard = 4096
+    buf = torch.full((n * m + 2 * guard + 1,), 7.0, dtype=torch.float32, device=dev())
+    y = buf[guard + 1: guard + 1 + n * m].view(n, m)
+    assert y.data_ptr() % 16 == 4
+    got = gpu_forward(x, k, y=y)
+    assert_forward_equal(got, oracle.maxk_forward(x, k), f"misaligned m={m}")
+    host = buf.cpu().numpy()
+    assert np.all(host[:guard + 1] == 7.0) and np.all(host[guard + 1 + n * m:] == 7.0)
+
+
+def test_forward_then_backward_round_trip():
+    # Backward of the forward's survivors with the survivors as gradient
+    # reproduces the dense forward output.
+    x = workloads.config_input(3, 8192, 256)
+    y, v, i = gpu_forward(x, 32, u8=True)
+    back = gpu_backward(v, i, 256, u8=True)
+    assert_bits_equal(back, y, "round trip")
+
+
+def test_forward_full_headline_shape():
+    n, m, k = 262144, 256, 32
+    x = workloads.config_input(3, n, m)
+    assert_forward_equal(gpu_forward(x, k, u8=True), oracle.maxk_forward(x, k),
+                         "262144 x 256 u8")
