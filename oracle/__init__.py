@@ -11,6 +11,8 @@ survivors per row), ties at the k-th value going to the lowest indices.
 ``capped`` is the threshold search with early stopping and tie fill of the RTop-K
 summary page, "Approach", in the reading spelled out in ``rtopk_oracle.cpp``.
 Both return the survivors of each row in ascending index order.
+``bucketed`` is the bucketed approximate top-k (page "Approximate Top-k for
+Increased Parallelism"): exact top-(k/b) of each of b contiguous buckets.
 ``maxk_forward`` / ``maxk_backward`` are the MaxK nonlinearity of the MaxK-GNN
 review ("How MaxK-GNN works"): the dense [N, M] output that keeps each row's
 exact top-k and zeroes the rest, and the gradient that flows back only to the
@@ -60,6 +62,9 @@ def _load():
                                   ctypes.c_float, ctypes.c_int32, f32p, i32p,
                                   i32p, f32p, f32p]
     lib.oracle_capped.restype = ctypes.c_int
+    lib.oracle_bucketed.argtypes = [f32p, ctypes.c_int64, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_int32, f32p, i32p]
+    lib.oracle_bucketed.restype = ctypes.c_int
     lib.oracle_maxk_forward.argtypes = [f32p, ctypes.c_int64, ctypes.c_int32,
                                         ctypes.c_int32, f32p, f32p, i32p]
     lib.oracle_maxk_forward.restype = ctypes.c_int
@@ -122,6 +127,18 @@ def capped(x, k: int, max_iter: int = -1, eps: float = 0.0,
             f"oracle_capped: invalid arguments (N={n}, M={m}, k={k}, eps={eps})")
     if return_state:
         return vals, idx, counts, lo, hi
+    return vals, idx
+
+
+def bucketed(x, k: int, buckets: int):
+    """Bucketed top-k: (values [N,k] f32, indices [N,k] i32), bucket by bucket."""
+    x = _as_rows(x)
+    n, m = x.shape
+    vals = np.empty((n, k), dtype=np.float32)
+    idx = np.empty((n, k), dtype=np.int32)
+    rc = _load().oracle_bucketed(_fp(x), n, m, k, int(buckets), _fp(vals), _ip(idx))
+    if rc != 0:
+        raise ValueError(f"oracle_bucketed: invalid arguments (N={n}, M={m}, k={k}, buckets={buckets})")
     return vals, idx
 
 

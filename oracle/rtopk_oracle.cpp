@@ -24,6 +24,15 @@
 //                     back to its column through the same sp_index and leaves
 //                     every other column at zero.
 //
+//   oracle_bucketed -- bucketed approximate top-k (page "Approximate Top-k for
+//                     Increased Parallelism", abstract: many small top-k
+//                     selections computed independently in place of one). The
+//                     page gives no layout; read here as: the row is cut into
+//                     `buckets` contiguous buckets of M / buckets columns, each
+//                     bucket keeps its exact top (k / buckets) by the rule of
+//                     oracle_exact, and the survivors are listed bucket by
+//                     bucket (hence in ascending column order).
+//
 //   oracle_capped  -- the threshold search of the RTop-K summary page, section
 //                     "Approach": bisection over the row's value range until a
 //                     threshold selects k elements, an optional cap on the
@@ -188,6 +197,26 @@ int oracle_capped(const float* x, int64_t N, int32_t M, int32_t k,
     capped_row(x + r * M, M, k, max_iter, eps, fill_from_row_min,
                out_val + r * k, out_idx + r * k, counts ? counts + r : nullptr,
                lo_out ? lo_out + r : nullptr, hi_out ? hi_out + r : nullptr);
+  }
+  return 0;
+}
+
+// Bucketed top-k (see the header). Requires buckets >= 1, M % buckets == 0,
+// k % buckets == 0 and 1 <= k <= M. Returns 0, or 1 on invalid arguments.
+int oracle_bucketed(const float* x, int64_t N, int32_t M, int32_t k,
+                    int32_t buckets, float* out_val, int32_t* out_idx) {
+  if (N < 0 || M < 1 || k < 1 || k > M || buckets < 1) return 1;
+  if (M % buckets != 0 || k % buckets != 0) return 1;
+  const int width = M / buckets;
+  const int keep = k / buckets;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < N; ++r) {
+    for (int b = 0; b < buckets; ++b) {
+      float* ov = out_val + r * k + b * keep;
+      int32_t* oi = out_idx + r * k + b * keep;
+      exact_row(x + r * M + b * width, width, keep, ov, oi);
+      for (int i = 0; i < keep; ++i) oi[i] += b * width;
+    }
   }
   return 0;
 }
