@@ -109,6 +109,9 @@ def record_traffic(workload: str, kernel: str, fetch_csv: str, write_csv: str) -
 def workload_name(args) -> str:
     if args.op in ("maxk_backward", "maxk_forward"):
         return f"{args.op} {args.inputs} N={args.rows} M={args.m} k={args.k} idx={args.index}"
+    if args.op == "bucketed":
+        return (f"bucketed {args.inputs} N={args.rows} M={args.m} k={args.k} "
+                f"buckets={args.buckets} idx={args.index}")
     return (f"{args.inputs} N={args.rows} M={args.m} k={args.k} {args.mode}"
             + ("" if args.mode == "exact" else f" max_iter={args.max_iter} eps={args.eps}")
             + f" idx={args.index}")
@@ -116,13 +119,13 @@ def workload_name(args) -> str:
 
 # Name fragment of the kernel each op launches (for the counter records).
 OP_KERNEL = {"select": "rows_in_registers", "maxk_forward": "rows_in_registers",
-             "maxk_backward": "scatter_rows"}
+             "maxk_backward": "scatter_rows", "bucketed": "rows_in_registers"}
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--op", choices=["select", "maxk_forward", "maxk_backward"],
+    p.add_argument("--op", choices=["select", "maxk_forward", "maxk_backward", "bucketed"],
                    default="select",
                    help="select: row-wise top-k (the headline); maxk_forward: "
                         "the MaxK nonlinearity (dense output plus the compressed "
@@ -132,6 +135,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=300,
                    help="untimed launches first; the GPU's clocks take about "
                         "150 launches (~10 ms) of sustained load to settle")
+    p.add_argument("--buckets", type=int, default=8,
+                   help="buckets per row for --op bucketed")
     p.add_argument("--rows", type=int, default=262144)
     p.add_argument("--m", type=int, default=256)
     p.add_argument("--k", type=int, default=32)
@@ -213,6 +218,10 @@ def main():
         def step(i):
             rt.rtopk_maxk_backward(grads[i % nbuf], idxs[i % nbuf], m,
                                    grad_x=outs[i % nout])
+    elif args.op == "bucketed":
+        def step(i):
+            rt.rtopk_select_bucketed(xs[i % nbuf], k, args.buckets, out_val=out_v,
+                                     out_idx=out_i, index_dtype=idx_dtype)
     elif args.op == "maxk_forward":
         nout = max(1, -(-768 * 2**20 // (n * m * 4)))
         ys = [torch.empty((n, m), dtype=torch.float32, device=dev) for _ in range(nout)]
@@ -300,6 +309,16 @@ def main():
     workload = workload_name(args)
     traffic = measured_traffic(workload)
 
+    # Approximate ops: hit rate and relative errors against the library's exact
+    # selection of the same rows (definitions in row_wise_top_amd/quality.py).
+    quality = None
+    if args.op == "bucketed" or (args.op == "select" and args.mode == "capped"):
+        from row_wise_top_amd.quality import topk_quality
+        step(0)
+        ev, _ = rt.rtopk_select_exact(xs[0], k)
+        torch.cuda.synchronize()
+        quality = topk_quality(out_v.cpu().numpy(), ev.cpu().numpy())
+
     cpu = None
     if args.cpu_seconds > 0:
         import oracle
@@ -314,6 +333,8 @@ def main():
                 oracle.maxk_backward(g_np, i_np, m)
             elif args.op == "maxk_forward":
                 oracle.maxk_forward(x_np, k)
+            elif args.op == "bucketed":
+                oracle.bucketed(x_np, k, args.buckets)
             elif args.mode == "exact":
                 oracle.exact(x_np, k)
             else:
@@ -326,9 +347,11 @@ def main():
                          f"({t_cpu:.1f} s of oracle time)"}
 
     line = {
-        "metric": METRIC if args.op == "select" else
-                  f"rows/sec and achieved HBM GB/s (% of peak), MaxK "
-                  f"{args.op.split('_')[1]} N={n} M={m} k={k} fp32",
+        "metric": (METRIC if args.op == "select" else
+                   f"rows/sec and achieved HBM GB/s (% of peak), bucketed top-k "
+                   f"N={n} M={m} k={k} buckets={args.buckets} fp32" if args.op == "bucketed" else
+                   f"rows/sec and achieved HBM GB/s (% of peak), MaxK "
+                   f"{args.op.split('_')[1]} N={n} M={m} k={k} fp32"),
         "value": n / (ms_per_step * 1e-3),
         "unit": "rows/s",
         "n_gpus": 1,
@@ -353,6 +376,8 @@ def main():
                              "launches": n_single},
         "stream_copy_gbs": copy_gbs,
     }
+    if quality is not None:
+        line["quality_vs_exact"] = quality
     print(json.dumps(line), flush=True)
 
 

@@ -38,8 +38,9 @@
  * caller's next synchronisation, as for any HIP launch.
  *
  * Errors. RTOPK_ERROR_INVALID_VALUE: a NULL pointer (when N > 0), N < 0,
- * M < 1, k < 1, k > M, eps < 0 or NaN. RTOPK_ERROR_NOT_SUPPORTED:
- * M > RTOPK_MAX_ROW_LENGTH, or a _u8 form with M > 256. RTOPK_ERROR_LAUNCH:
+ * M < 1, k < 1, k > M, eps < 0 or NaN (and the bucket conditions below).
+ * RTOPK_ERROR_NOT_SUPPORTED: M > RTOPK_MAX_ROW_LENGTH, or a _u8 form with
+ * M > 256 (and buckets longer than 1024). RTOPK_ERROR_LAUNCH:
  * the HIP runtime reported an error while enqueuing. On any error nothing is
  * enqueued and the outputs are untouched.
  */
@@ -103,6 +104,29 @@ rtopk_status_t rtopk_select_u8(const float* x, int64_t N, int32_t M, int32_t k,
 rtopk_status_t rtopk_select_exact_u8(const float* x, int64_t N, int32_t M,
                                      int32_t k, float* out_val,
                                      uint8_t* out_idx, hipStream_t stream);
+
+/*
+ * Bucketed approximate top-k (page "Approximate Top-k for Increased
+ * Parallelism": independent small top-k selections in place of one). Each
+ * row is cut into `buckets` contiguous buckets of M / buckets columns, each
+ * bucket keeps its exact top (k / buckets) (ties to the lowest columns), and
+ * the k survivors are written bucket by bucket, i.e. in ascending column
+ * order, with columns relative to the whole row.
+ *   buckets  1 <= buckets, M % buckets == 0 and k % buckets == 0
+ *            (else RTOPK_ERROR_INVALID_VALUE); M / buckets <= 1024 (else
+ *            RTOPK_ERROR_NOT_SUPPORTED).
+ * Everything else is as for rtopk_select_exact; buckets == 1 is the exact
+ * top-k.
+ */
+rtopk_status_t rtopk_select_bucketed(const float* x, int64_t N, int32_t M,
+                                     int32_t k, int32_t buckets, float* out_val,
+                                     int32_t* out_idx, hipStream_t stream);
+
+/* As rtopk_select_bucketed with one-byte column indices. Requires M <= 256. */
+rtopk_status_t rtopk_select_bucketed_u8(const float* x, int64_t N, int32_t M,
+                                        int32_t k, int32_t buckets,
+                                        float* out_val, uint8_t* out_idx,
+                                        hipStream_t stream);
 
 /*
  * MaxK nonlinearity, forward (MaxK-GNN review, "How MaxK-GNN works": each row

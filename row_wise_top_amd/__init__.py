@@ -10,11 +10,13 @@ include/rtopk.h (librtopk.so); this package is a thin binding over it.
 from __future__ import annotations
 
 from ._lib import (RTOPK_MAX_ROW_LENGTH, lib, rtopk_maxk_backward,
-                   rtopk_maxk_forward, rtopk_select, rtopk_select_exact,
-                   rtopk_select_exact_u8, rtopk_select_u8, rtopk_status_string)
+                   rtopk_maxk_forward, rtopk_select, rtopk_select_bucketed,
+                   rtopk_select_exact, rtopk_select_exact_u8, rtopk_select_u8,
+                   rtopk_status_string)
 
 __all__ = ["select", "lib", "rtopk_select", "rtopk_select_exact",
-           "rtopk_select_u8", "rtopk_select_exact_u8", "rtopk_maxk_forward",
+           "rtopk_select_u8", "rtopk_select_exact_u8", "rtopk_select_bucketed",
+           "rtopk_maxk_forward",
            "rtopk_maxk_backward",
            "rtopk_status_string", "RTOPK_MAX_ROW_LENGTH"]
 

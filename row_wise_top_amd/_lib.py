@@ -39,12 +39,15 @@ def lib() -> ctypes.CDLL:
     l.rtopk_select_u8.argtypes = [vp, i64, i32, i32, i32, f32, vp, vp, vp]
     l.rtopk_select_exact.argtypes = [vp, i64, i32, i32, vp, vp, vp]
     l.rtopk_select_exact_u8.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+    l.rtopk_select_bucketed.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp]
+    l.rtopk_select_bucketed_u8.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp]
     l.rtopk_maxk_forward.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
     l.rtopk_maxk_forward_u8.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
     l.rtopk_maxk_backward.argtypes = [vp, vp, i64, i32, i32, vp, vp]
     l.rtopk_maxk_backward_u8.argtypes = [vp, vp, i64, i32, i32, vp, vp]
     for f in (l.rtopk_select, l.rtopk_select_u8, l.rtopk_select_exact,
-              l.rtopk_select_exact_u8, l.rtopk_maxk_forward,
+              l.rtopk_select_exact_u8, l.rtopk_select_bucketed,
+              l.rtopk_select_bucketed_u8, l.rtopk_maxk_forward,
               l.rtopk_maxk_forward_u8, l.rtopk_maxk_backward,
               l.rtopk_maxk_backward_u8):
         f.restype = ctypes.c_int
@@ -133,6 +136,24 @@ def rtopk_select_exact_u8(x, k: int, out_val=None, out_idx=None, stream=None):
     _check(lib().rtopk_select_exact_u8(x.data_ptr(), n, m, k, out_val.data_ptr(),
                                        out_idx.data_ptr(), _stream(x, stream)),
            "rtopk_select_exact_u8")
+    return out_val, out_idx
+
+
+def rtopk_select_bucketed(x, k: int, buckets: int, out_val=None, out_idx=None,
+                          index_dtype=None, stream=None):
+    """Bucketed top-k: the exact top-(k/buckets) of each of `buckets`
+    contiguous buckets of every row, columns relative to the row, bucket by
+    bucket. index_dtype: torch.int32 (default) or torch.uint8 (M <= 256)."""
+    import torch
+    idx_dtype = torch.int32 if index_dtype is None else index_dtype
+    if idx_dtype not in (torch.int32, torch.uint8):
+        raise ValueError("index_dtype must be torch.int32 or torch.uint8")
+    n, m, out_val, out_idx = _prepare(x, k, out_val, out_idx, idx_dtype)
+    u8 = idx_dtype == torch.uint8
+    fn = lib().rtopk_select_bucketed_u8 if u8 else lib().rtopk_select_bucketed
+    _check(fn(x.data_ptr(), n, m, k, int(buckets), out_val.data_ptr(),
+              out_idx.data_ptr(), _stream(x, stream)),
+           "rtopk_select_bucketed_u8" if u8 else "rtopk_select_bucketed")
     return out_val, out_idx
 
 

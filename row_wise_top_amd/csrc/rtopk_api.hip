@@ -30,7 +30,7 @@ rtopk_status_t run(const float* x, int64_t n, int32_t m, int32_t k,
       validate(x, n, m, k, eps, out_val, out_idx, u8_index);
   if (st != RTOPK_SUCCESS) return st;
   if (n == 0) return RTOPK_SUCCESS;
-  rtopk::SelectArgs a{x, n, m, k, max_iter, eps, out_val, out_idx, 0.0f, 0.0f, nullptr};
+  rtopk::SelectArgs a{x, n, m, k, max_iter, eps, out_val, out_idx, 0.0f, 0.0f, nullptr, 1};
   const hipError_t err = rtopk::launch_select(a, mode, u8_index, stream);
   return err == hipSuccess ? RTOPK_SUCCESS : RTOPK_ERROR_LAUNCH;
 }
@@ -61,7 +61,7 @@ rtopk_status_t run_maxk_forward(const float* x, int64_t n, int32_t m, int32_t k,
   if (n > 0 && y == nullptr) return RTOPK_ERROR_INVALID_VALUE;
   if (n == 0) return RTOPK_SUCCESS;
   const int q = (m + rtopk::kWave - 1) / rtopk::kWave;
-  rtopk::SelectArgs a{x, n, m, k, -1, 0.0f, sp_data, sp_index, 0.0f, 0.0f, y};
+  rtopk::SelectArgs a{x, n, m, k, -1, 0.0f, sp_data, sp_index, 0.0f, 0.0f, y, 1};
   hipError_t err;
   if (rtopk::maxk_fused(q)) {
     err = rtopk::launch_select(a, rtopk::Mode::kMaxk, u8_index, stream);
@@ -73,6 +73,28 @@ rtopk_status_t run_maxk_forward(const float* x, int64_t n, int32_t m, int32_t k,
       err = rtopk::launch_scatter(s, u8_index, stream);
     }
   }
+  return err == hipSuccess ? RTOPK_SUCCESS : RTOPK_ERROR_LAUNCH;
+}
+
+// Bucketed top-k: the exact kernel over the [n * buckets, m / buckets] view
+// of x (each bucket a row, k / buckets survivors), emitted columns offset by
+// the bucket's position; the [n, k] outputs are the [n * buckets,
+// k / buckets] outputs of that view.
+rtopk_status_t run_bucketed(const float* x, int64_t n, int32_t m, int32_t k,
+                            int32_t buckets, float* out_val, void* out_idx,
+                            bool u8_index, hipStream_t stream) {
+  const rtopk_status_t st = validate(x, n, m, k, 0.0f, out_val, out_idx, u8_index);
+  if (st != RTOPK_SUCCESS) return st;
+  if (buckets < 1 || m % buckets != 0 || k % buckets != 0)
+    return RTOPK_ERROR_INVALID_VALUE;
+  const int32_t width = m / buckets;
+  if (!rtopk::bucket_supported((width + rtopk::kWave - 1) / rtopk::kWave))
+    return RTOPK_ERROR_NOT_SUPPORTED;
+  if (n > INT64_MAX / buckets) return RTOPK_ERROR_NOT_SUPPORTED;
+  if (n == 0) return RTOPK_SUCCESS;
+  rtopk::SelectArgs a{x,       n * buckets, width, k / buckets, -1, 0.0f,
+                      out_val, out_idx,     0.0f,  0.0f,        nullptr, buckets};
+  const hipError_t err = rtopk::launch_select(a, rtopk::Mode::kBucket, u8_index, stream);
   return err == hipSuccess ? RTOPK_SUCCESS : RTOPK_ERROR_LAUNCH;
 }
 
@@ -108,6 +130,19 @@ rtopk_status_t rtopk_select_exact_u8(const float* x, int64_t N, int32_t M,
              rtopk::Mode::kExact, stream);
 }
 
+rtopk_status_t rtopk_select_bucketed(const float* x, int64_t N, int32_t M,
+                                     int32_t k, int32_t buckets, float* out_val,
+                                     int32_t* out_idx, hipStream_t stream) {
+  return run_bucketed(x, N, M, k, buckets, out_val, out_idx, false, stream);
+}
+
+rtopk_status_t rtopk_select_bucketed_u8(const float* x, int64_t N, int32_t M,
+                                        int32_t k, int32_t buckets,
+                                        float* out_val, uint8_t* out_idx,
+                                        hipStream_t stream) {
+  return run_bucketed(x, N, M, k, buckets, out_val, out_idx, true, stream);
+}
+
 rtopk_status_t rtopk_maxk_forward(const float* x, int64_t N, int32_t M,
                                   int32_t k, float* y, float* sp_data,
                                   int32_t* sp_index, hipStream_t stream) {
@@ -139,9 +174,11 @@ const char* rtopk_status_string(rtopk_status_t status) {
     case RTOPK_SUCCESS:
       return "success";
     case RTOPK_ERROR_INVALID_VALUE:
-      return "invalid value: null pointer, N < 0, M < 1, k < 1, k > M, or eps < 0 / NaN";
+      return "invalid value: null pointer, N < 0, M < 1, k < 1, k > M, eps < 0 / NaN, "
+             "or buckets that do not divide M and k";
     case RTOPK_ERROR_NOT_SUPPORTED:
-      return "not supported: M > 8192, or one-byte indices with M > 256";
+      return "not supported: M > 8192, one-byte indices with M > 256, or buckets "
+             "longer than 1024";
     case RTOPK_ERROR_LAUNCH:
       return "kernel launch failed";
   }

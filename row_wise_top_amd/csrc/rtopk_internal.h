@@ -15,7 +15,10 @@ constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = kWave * kWavesPerBlock;
 
 // kMaxk: the exact search, plus the dense [n, m] MaxK output (SelectArgs::dense).
-enum class Mode { kCapped, kExact, kMaxk };
+// kBucket: the exact search on buckets: each kernel row is one bucket of an
+// input row (SelectArgs::buckets of them, m columns each) and emitted
+// columns are offset by the bucket's position in its row.
+enum class Mode { kCapped, kExact, kMaxk, kBucket };
 
 struct SelectArgs {
   const float* x;
@@ -32,6 +35,7 @@ struct SelectArgs {
   float z_first;     // first threshold = r * z_first
   float half_step;   // Newton step per doubled count = r * half_step
   float* dense;      // Mode::kMaxk only: [n, m] output, survivors kept, rest 0
+  int32_t buckets;   // Mode::kBucket only: buckets per input row (>= 1)
 };
 
 using RowsKernel = void (*)(SelectArgs);
@@ -48,6 +52,9 @@ constexpr bool one_group_per_wave(int q) { return q <= 16; }
 // Rows the fused MaxK forward kernel takes (its LDS holds the dense row);
 // longer rows run the selection and then the scatter.
 constexpr bool maxk_fused(int q) { return q <= 16; }
+
+// Bucket lengths the bucketed kernels take (64*q columns, q <= 16).
+constexpr bool bucket_supported(int q) { return q <= 16; }
 
 // Slot counts Q (elements per lane) with an instantiated register-resident
 // row kernel; a row of length m uses the smallest Q with 64*Q >= m.

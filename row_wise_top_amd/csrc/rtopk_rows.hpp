@@ -216,31 +216,36 @@ constexpr int kRsrcWord3 = 0x00020000;
 // four still a valid 32-bit offset.
 constexpr uint32_t kDropPos = 1u << 28;
 
-// DENSE (MaxK forward): every survivor is also written, as value bits, to
-// its column of the wave's LDS copy of the dense row (zeroed before the row
-// and stored after it); lanes not selected write their spare word instead.
-template <typename IdxT, bool DENSE>
+// Mode::kMaxk: every survivor is also written, as value bits, to its column
+// of the wave's LDS copy of the dense row (zeroed before the row and stored
+// after it); lanes not selected write their spare word instead.
+// Mode::kBucket: emitted columns are offset by the bucket's first column.
+template <typename IdxT, Mode MODE>
 struct OutRow {
   __amdgpu_buffer_rsrc_t val;
   __amdgpu_buffer_rsrc_t idx;
-  uint32_t* dense;  // DENSE only: the LDS row (plus one spare word per lane)
-  uint32_t spare;   // DENSE only: this lane's spare word
+  uint32_t* dense;   // kMaxk only: the LDS row (plus one spare word per lane)
+  uint32_t spare;    // kMaxk only: this lane's spare word
+  int col_base;      // kBucket only: column of the bucket's first element
 
   __device__ __forceinline__ OutRow(float* ov, IdxT* oi, int k,
-                                    uint32_t* dense_row, uint32_t spare_word)
+                                    uint32_t* dense_row, uint32_t spare_word,
+                                    int first_col)
       : val(__builtin_amdgcn_make_buffer_rsrc(ov, 0, k * 4, kRsrcWord3)),
         idx(__builtin_amdgcn_make_buffer_rsrc(
             oi, 0, k * static_cast<int>(sizeof(IdxT)), kRsrcWord3)),
         dense(dense_row),
-        spare(spare_word) {}
+        spare(spare_word),
+        col_base(first_col) {}
 
   // Lanes whose bit of `msk` is set emit (x, col) as entry `rank` of the row;
   // the others store nothing.
   __device__ __forceinline__ void put(uint64_t msk, uint32_t rank, float x,
                                       int col) const {
     const uint32_t pos = lane_select(msk, rank, kDropPos);
-    if constexpr (DENSE)
+    if constexpr (MODE == Mode::kMaxk)
       dense[lane_select(msk, static_cast<uint32_t>(col), spare)] = __float_as_uint(x);
+    if constexpr (MODE == Mode::kBucket) col += col_base;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), val,
                                           static_cast<int>(pos * 4u), 0, 0);
     if constexpr (sizeof(IdxT) == 1) {
@@ -720,6 +725,12 @@ __global__ __launch_bounds__(kBlock) void rows_in_registers(SelectArgs a) {
   float* og = a.out_val + r * k;
   IdxT* ig = static_cast<IdxT*>(a.out_idx) + r * k;
   float* yg = kDense ? a.dense + r * m : nullptr;
+  // kBucket: bucket index of row r within its input row, and the group's
+  // first row (rows within a group are consecutive, so the index advances
+  // with a wrap; one 64-bit remainder per group).
+  constexpr bool kBuckets = MODE == Mode::kBucket;
+  int64_t rg = r;
+  int bucket = kBuckets ? static_cast<int>(r % a.buckets) : 0;
   float buf[D][Q];
   // Unconditional loads (rows past this wave's last one re-read its last
   // row) so that the compiler's wait counts need no worst-case assumption.
@@ -745,7 +756,9 @@ __global__ __launch_bounds__(kBlock) void rows_in_registers(SelectArgs a) {
       }
       process_row<Q, FULL, MODE, QC>(
           buf[d], a, lane, scratch,
-          OutRow<IdxT, kDense>(og + d * k, ig + d * k, a.k, dense, spare));
+          OutRow<IdxT, MODE>(og + d * k, ig + d * k, a.k, dense, spare,
+                             bucket * a.m));
+      if constexpr (kBuckets) bucket = bucket + 1 == a.buckets ? 0 : bucket + 1;
       if constexpr (kDense) {
         __builtin_amdgcn_wave_barrier();
         // The dense row, stores past its end dropped.
@@ -764,6 +777,10 @@ __global__ __launch_bounds__(kBlock) void rows_in_registers(SelectArgs a) {
     og += group_rows * k;
     ig += group_rows * k;
     if constexpr (kDense) yg += group_rows * m;
+    if constexpr (kBuckets) {
+      rg += group_rows;
+      bucket = static_cast<int>(rg % a.buckets);
+    }
   }
 }
 
@@ -805,6 +822,10 @@ RowsKernel any_kernel(Mode mode, int qc) {
     if constexpr (maxk_fused(Q)) return exact_kernel<Q, FULL, Mode::kMaxk, IdxT>(qc);
     return nullptr;
   }
+  if (mode == Mode::kBucket) {
+    if constexpr (bucket_supported(Q)) return exact_kernel<Q, FULL, Mode::kBucket, IdxT>(qc);
+    return nullptr;
+  }
   return rows_in_registers<Q, FULL, Mode::kCapped, 0, IdxT>;
 }
 
@@ -814,7 +835,7 @@ RowsKernel any_kernel(Mode mode, int qc) {
 // buckets listed in rtopk_internal.h. full: the row length is exactly 64*Q
 // (only distinguished for Q <= 4). qc: candidate slots for the exact search
 // (see candidate_slots). Returns nullptr for one-byte indices with Q > 4,
-// and for Mode::kMaxk with rows too long for the fused kernel.
+// and for Mode::kMaxk / kBucket with rows too long for those kernels.
 template <int Q>
 RowsKernel rows_kernel(bool full, Mode mode, bool u8_index, int qc) {
   using rows_detail::any_kernel;

@@ -23,7 +23,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted([
         "rtopk_select", "rtopk_select_exact", "rtopk_select_u8",
-        "rtopk_select_exact_u8", "rtopk_maxk_forward", "rtopk_maxk_forward_u8",
+        "rtopk_select_exact_u8", "rtopk_select_bucketed", "rtopk_select_bucketed_u8",
+        "rtopk_maxk_forward", "rtopk_maxk_forward_u8",
         "rtopk_maxk_backward", "rtopk_maxk_backward_u8", "rtopk_status_string"])
 
 
@@ -158,3 +159,37 @@ def test_forward_null_pointers(fn, which):
     ptrs = [FAKE, FAKE, FAKE, FAKE]
     ptrs[which] = None
     assert call(fn, ptrs[0], 4, 16, 4, ptrs[1], ptrs[2], ptrs[3], None) == 1
+
+
+BUCKETED = ["rtopk_select_bucketed", "rtopk_select_bucketed_u8"]
+
+
+@pytest.mark.parametrize("fn", BUCKETED)
+def test_bucketed_n_zero_is_a_noop(fn):
+    assert call(fn, None, 0, 16, 4, 2, None, None, None) == 0
+
+
+@pytest.mark.parametrize("fn", BUCKETED)
+@pytest.mark.parametrize("n,m,k,b,code", [
+    (-1, 16, 4, 2, 1),      # N < 0
+    (4, 16, 17, 1, 1),      # k > M
+    (4, 16, 4, 0, 1),       # no buckets
+    (4, 16, 4, 3, 1),       # 3 does not divide M
+    (4, 18, 4, 3, 1),       # 3 does not divide k
+    (4, 8193, 4, 1, 2),     # M above the maximum
+])
+def test_bucketed_argument_errors(fn, n, m, k, b, code):
+    assert call(fn, FAKE, n, m, k, b, FAKE, FAKE, None) == code
+
+
+def test_bucketed_long_buckets_not_supported():
+    assert call("rtopk_select_bucketed", FAKE, 4, 2048, 8, 1, FAKE, FAKE, None) == 2
+    assert call("rtopk_select_bucketed_u8", FAKE, 4, 512, 8, 2, FAKE, FAKE, None) == 2
+
+
+@pytest.mark.parametrize("fn", BUCKETED)
+@pytest.mark.parametrize("which", [0, 1, 2])
+def test_bucketed_null_pointers(fn, which):
+    ptrs = [FAKE, FAKE, FAKE]
+    ptrs[which] = None
+    assert call(fn, ptrs[0], 4, 16, 4, 2, ptrs[1], ptrs[2], None) == 1

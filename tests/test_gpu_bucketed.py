@@ -1,0 +1,76 @@
+"""GPU parity of the bucketed approximate top-k (rtopk_select_bucketed[_u8])
+against oracle.bucketed, bit for bit: the same columns (relative to the whole
+row, bucket by bucket) and the same value bits. Bucket lengths cover every
+slot bucket of the kernels up to 1024, ragged bucket lengths, ties and the
+full 262,144 x 256 shape with 8 buckets."""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def gpu_bucketed(x_np, k, b, u8=False):
+    import row_wise_top_amd as rt
+    x = torch.from_numpy(np.ascontiguousarray(x_np)).to("cuda:0")
+    v, i = rt.rtopk_select_bucketed(x, k, b, index_dtype=torch.uint8 if u8 else None)
+    torch.cuda.synchronize()
+    return v.cpu().numpy(), i.cpu().numpy().astype(np.int32)
+
+
+def assert_identical(got, want, label):
+    gv, gi = got
+    wv, wi = want
+    bad = np.flatnonzero((gi != wi).any(axis=1) |
+                         (gv.view(np.uint32) != wv.view(np.uint32)).any(axis=1))
+    assert bad.size == 0, f"{label}: {bad.size} rows differ, first {bad[0]}"
+
+
+CASES = [  # (n, m, k, buckets)
+    (100, 8, 4, 2), (257, 64, 8, 2), (300, 100, 20, 5), (129, 256, 32, 8),
+    (500, 256, 32, 4), (77, 256, 64, 2), (64, 256, 256, 256), (99, 256, 16, 16),
+    (60, 384, 24, 3), (50, 1000, 40, 4), (40, 1024, 64, 1), (33, 2048, 64, 2),
+    (20, 3072, 48, 3), (17, 8192, 64, 8), (9, 8192, 512, 8),
+]
+
+
+@pytest.mark.parametrize("n,m,k,b", CASES)
+@pytest.mark.parametrize("data", ["normal", "maxk", "grid"])
+def test_bucketed_matches_oracle(n, m, k, b, data):
+    if data == "normal":
+        x = workloads.normal(n, m, 500 + m + b)
+    elif data == "maxk":
+        x = workloads.maxk_activation(n, m, workloads.CONFIG_SEEDS[3])
+    else:
+        x = workloads.grid_ties(n, m, 5)
+    want = oracle.bucketed(x, k, b)
+    assert_identical(gpu_bucketed(x, k, b), want, f"i32 {data} n={n} m={m} k={k} b={b}")
+    if m <= 256:
+        assert_identical(gpu_bucketed(x, k, b, u8=True), want, f"u8 {data} n={n} m={m} k={k} b={b}")
+
+
+@pytest.mark.parametrize("m,b", [(6, 3), (100, 4), (256, 8), (1024, 2)])
+def test_bucketed_adversarial_rows(m, b):
+    x = workloads.adversarial_rows(m)
+    for k in sorted({b, 2 * b if 2 * b <= m else b, m}):
+        if k % b:
+            continue
+        assert_identical(gpu_bucketed(x, k, b), oracle.bucketed(x, k, b),
+                         f"adversarial m={m} b={b} k={k}")
+
+
+def test_bucketed_ragged_row_counts():
+    for n in (1, 2, 3, 5, 17, 1023, 1025):
+        x = workloads.normal(n, 256, 600 + n)
+        assert_identical(gpu_bucketed(x, 32, 8, u8=True), oracle.bucketed(x, 32, 8), f"n={n}")
+
+
+def test_bucketed_full_shape():
+    x = workloads.config_input(3, 262144, 256)
+    assert_identical(gpu_bucketed(x, 32, 8, u8=True), oracle.bucketed(x, 32, 8),
+                     "262144 x 256 k=32 b=8")
