@@ -13,6 +13,8 @@ summary page, "Approach", in the reading spelled out in ``rtopk_oracle.cpp``.
 Both return the survivors of each row in ascending index order.
 ``bucketed`` is the bucketed approximate top-k (page "Approximate Top-k for
 Increased Parallelism"): exact top-(k/b) of each of b contiguous buckets.
+``spgemm`` is MaxK-GNN's forward aggregation Y = A X (CSR graph A, X given
+by its compressed MaxK rows), summed in double and rounded once.
 ``maxk_forward`` / ``maxk_backward`` are the MaxK nonlinearity of the MaxK-GNN
 review ("How MaxK-GNN works"): the dense [N, M] output that keeps each row's
 exact top-k and zeroes the rest, and the gradient that flows back only to the
@@ -71,6 +73,11 @@ def _load():
     lib.oracle_maxk_backward.argtypes = [f32p, i32p, ctypes.c_int64,
                                          ctypes.c_int32, ctypes.c_int32, f32p]
     lib.oracle_maxk_backward.restype = ctypes.c_int
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.oracle_spgemm.argtypes = [i64p, i32p, f32p, ctypes.c_int64, ctypes.c_int64,
+                                  f32p, i32p, ctypes.c_int32, ctypes.c_int32,
+                                  f32p, f32p]
+    lib.oracle_spgemm.restype = ctypes.c_int
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
     _lib = lib
@@ -167,6 +174,29 @@ def maxk_backward(grad_sp, sp_index, m: int):
     if rc != 0:
         raise ValueError(f"oracle_maxk_backward: invalid arguments (N={n}, M={m}, k={k})")
     return out
+
+
+def spgemm(row_ptr, col_idx, val, n_src: int, sp_data, sp_index, m: int,
+           return_absum: bool = False):
+    """Y [n_dst, m] = A X; with ``return_absum`` also sum |a x| per element."""
+    rp = np.ascontiguousarray(row_ptr, dtype=np.int64)
+    ci = np.ascontiguousarray(col_idx, dtype=np.int32)
+    va = np.ascontiguousarray(val, dtype=np.float32)
+    sd = np.ascontiguousarray(sp_data, dtype=np.float32)
+    si = np.ascontiguousarray(sp_index, dtype=np.int32)
+    n_dst = rp.shape[0] - 1
+    k = sd.shape[1]
+    if sd.shape != si.shape or sd.shape[0] != n_src or ci.shape != va.shape:
+        raise ValueError("inconsistent shapes")
+    y = np.empty((n_dst, m), dtype=np.float32)
+    ab = np.empty((n_dst, m), dtype=np.float32) if return_absum else None
+    rc = _load().oracle_spgemm(
+        rp.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ip(ci), _fp(va),
+        n_dst, n_src, _fp(sd), _ip(si), m, k, _fp(y),
+        _fp(ab) if ab is not None else None)
+    if rc != 0:
+        raise ValueError("oracle_spgemm: invalid arguments")
+    return (y, ab) if return_absum else y
 
 
 def threads() -> int:

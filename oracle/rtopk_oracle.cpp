@@ -33,6 +33,14 @@
 //                     oracle_exact, and the survivors are listed bucket by
 //                     bucket (hence in ascending column order).
 //
+//   oracle_spgemm  -- the forward aggregation of MaxK-GNN (review page, "How
+//                     MaxK-GNN works"; abstract: row-wise product SpGEMM on
+//                     the compressed features): Y = A X with A a CSR graph and
+//                     X given as its compressed rows (k survivors of M
+//                     columns), i.e. Y[i, :] = sum over the edges e of row i
+//                     of val[e] * X[col[e], :]. Plain definition, summed in
+//                     double and rounded once.
+//
 //   oracle_capped  -- the threshold search of the RTop-K summary page, section
 //                     "Approach": bisection over the row's value range until a
 //                     threshold selects k elements, an optional cap on the
@@ -216,6 +224,39 @@ int oracle_bucketed(const float* x, int64_t N, int32_t M, int32_t k,
       int32_t* oi = out_idx + r * k + b * keep;
       exact_row(x + r * M + b * width, width, keep, ov, oi);
       for (int i = 0; i < keep; ++i) oi[i] += b * width;
+    }
+  }
+  return 0;
+}
+
+// Y[i, c] = sum over edges e in [row_ptr[i], row_ptr[i+1]) and entries t with
+// sp_index[col[e], t] == c of val[e] * sp_data[col[e], t], summed in double,
+// written as float. absum (optional, [n_dst, M]) receives the same sum of
+// |val * data|, rounded up, for error bounds. Edges whose column lies outside
+// [0, n_src) and entries outside [0, M) contribute nothing. Returns 0, or 1
+// on invalid arguments.
+int oracle_spgemm(const int64_t* row_ptr, const int32_t* col, const float* val,
+                  int64_t n_dst, int64_t n_src, const float* sp_data,
+                  const int32_t* sp_index, int32_t M, int32_t k, float* y,
+                  float* absum) {
+  if (n_dst < 0 || n_src < 0 || M < 1 || k < 1) return 1;
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t i = 0; i < n_dst; ++i) {
+    std::vector<double> acc(M, 0.0), mag(M, 0.0);
+    for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+      const int64_t j = col[e];
+      if (j < 0 || j >= n_src) continue;
+      for (int t = 0; t < k; ++t) {
+        const int32_t c = sp_index[j * k + t];
+        if (c < 0 || c >= M) continue;
+        const double term = static_cast<double>(val[e]) * static_cast<double>(sp_data[j * k + t]);
+        acc[c] += term;
+        mag[c] += term < 0 ? -term : term;
+      }
+    }
+    for (int c = 0; c < M; ++c) {
+      y[i * M + c] = static_cast<float>(acc[c]);
+      if (absum) absum[i * M + c] = static_cast<float>(mag[c] * (1.0 + 1e-6));
     }
   }
   return 0;

@@ -19,6 +19,14 @@ every -0.0 is replaced by +0.0 so that the inputs carry a single zero):
 * ``grid_ties``       x = round(4 z) / 4 with z ~ N(0, 1) (half-to-even
                       rounding): about 30 distinct values per row, so the k-th
                       value is almost always tied.
+* ``power_law_graph`` a CSR adjacency for the MaxK-GNN aggregation (review
+                      page: feature aggregation over graph edges, evaluated on
+                      high-degree graphs that are not available here): row
+                      degrees drawn from a power law with exponent 2.5
+                      (Pareto, x_min chosen for the requested mean), capped,
+                      with a fraction of empty rows; neighbours uniform over
+                      the source rows (repeats allowed); edge weight
+                      1 / degree of the row (mean aggregation).
 
 Named workloads (rows x row length, k, mode):
 
@@ -120,3 +128,23 @@ def adversarial_rows(m: int, seed: int = 11) -> np.ndarray:
     for _ in range(4):
         rows.append(rng.standard_normal(m).astype(f32))
     return np.ascontiguousarray(np.stack(rows).astype(np.float32))
+
+
+def power_law_graph(n_dst: int, n_src: int, mean_degree: float, max_degree: int,
+                    seed: int, exponent: float = 2.5, empty_frac: float = 0.01):
+    """(row_ptr int64 [n_dst + 1], col_idx int32 [E], val float32 [E])."""
+    rng = np.random.default_rng(seed)
+    # Uncapped Pareto mean is x_min * (a - 1) / (a - 2).
+    x_min = mean_degree * (exponent - 2.0) / (exponent - 1.0)
+    u = rng.random(n_dst)
+    deg = np.floor(x_min * (1.0 - u) ** (-1.0 / (exponent - 1.0))).astype(np.int64)
+    deg = np.clip(deg, 1, max_degree)
+    deg[rng.random(n_dst) < empty_frac] = 0
+    row_ptr = np.zeros(n_dst + 1, dtype=np.int64)
+    np.cumsum(deg, out=row_ptr[1:])
+    nnz = int(row_ptr[-1])
+    col_idx = rng.integers(0, n_src, size=nnz, dtype=np.int64).astype(np.int32)
+    inv = np.zeros(n_dst, dtype=np.float32)
+    inv[deg > 0] = (1.0 / deg[deg > 0]).astype(np.float32)
+    val = np.repeat(inv, deg).astype(np.float32)
+    return row_ptr, col_idx, val
