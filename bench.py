@@ -112,6 +112,9 @@ def workload_name(args) -> str:
     if args.op == "bucketed":
         return (f"bucketed {args.inputs} N={args.rows} M={args.m} k={args.k} "
                 f"buckets={args.buckets} idx={args.index}")
+    if args.op == "spgemm":
+        return (f"spgemm power-law graph N={args.rows} mean_degree={args.degree:g} "
+                f"M={args.m} k={args.k} idx={args.index}")
     return (f"{args.inputs} N={args.rows} M={args.m} k={args.k} {args.mode}"
             + ("" if args.mode == "exact" else f" max_iter={args.max_iter} eps={args.eps}")
             + f" idx={args.index}")
@@ -119,13 +122,15 @@ def workload_name(args) -> str:
 
 # Name fragment of the kernel each op launches (for the counter records).
 OP_KERNEL = {"select": "rows_in_registers", "maxk_forward": "rows_in_registers",
-             "maxk_backward": "scatter_rows", "bucketed": "rows_in_registers"}
+             "maxk_backward": "scatter_rows", "bucketed": "rows_in_registers",
+             "spgemm": "spgemm_rows"}
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--op", choices=["select", "maxk_forward", "maxk_backward", "bucketed"],
+    p.add_argument("--op", choices=["select", "maxk_forward", "maxk_backward", "bucketed",
+                                    "spgemm"],
                    default="select",
                    help="select: row-wise top-k (the headline); maxk_forward: "
                         "the MaxK nonlinearity (dense output plus the compressed "
@@ -135,6 +140,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=300,
                    help="untimed launches first; the GPU's clocks take about "
                         "150 launches (~10 ms) of sustained load to settle")
+    p.add_argument("--degree", type=float, default=64.0,
+                   help="mean degree of the power-law graph for --op spgemm")
     p.add_argument("--buckets", type=int, default=8,
                    help="buckets per row for --op bucketed")
     p.add_argument("--rows", type=int, default=262144)
@@ -218,6 +225,23 @@ def main():
         def step(i):
             rt.rtopk_maxk_backward(grads[i % nbuf], idxs[i % nbuf], m,
                                    grad_x=outs[i % nout])
+    elif args.op == "spgemm":
+        # A power-law graph over the same rows; features: the exact top-k of
+        # each rotated buffer (from the library's selection). Outputs rotate.
+        sel = rt.rtopk_select_exact_u8 if u8 else rt.rtopk_select_exact
+        feats = [sel(xb, k) for xb in xs]
+        del xs
+        rp_np, ci_np, va_np = workloads.power_law_graph(n, n, args.degree, 4096, seed=48)
+        nnz = int(ci_np.shape[0])
+        rp_t = torch.from_numpy(rp_np).to(dev)
+        ci_t = torch.from_numpy(ci_np).to(dev)
+        va_t = torch.from_numpy(va_np).to(dev)
+        nout = max(1, -(-768 * 2**20 // (n * m * 4)))
+        outs = [torch.empty((n, m), dtype=torch.float32, device=dev) for _ in range(nout)]
+
+        def step(i):
+            fv, fi = feats[i % nbuf]
+            rt.rtopk_cbsr_spgemm(rp_t, ci_t, va_t, fv, fi, m, y=outs[i % nout])
     elif args.op == "bucketed":
         def step(i):
             rt.rtopk_select_bucketed(xs[i % nbuf], k, args.buckets, out_val=out_v,
@@ -304,7 +328,18 @@ def main():
     # select and maxk_backward: M floats one way, k entries the other;
     # maxk_forward: M floats in, M floats and k entries out.
     per_row = 4 * m + k * (4 + idx_bytes) + (4 * m if args.op == "maxk_forward" else 0)
-    algo_bytes = n * per_row
+    extra = {}
+    if args.op == "spgemm":
+        # Bytes that must cross HBM at least once per launch: the CSR arrays,
+        # each feature row once, each output row once. The per-edge gathers
+        # of neighbour rows (nnz * k * (4 + b)) are served mostly by the
+        # last-level cache and reported separately.
+        per_row = 4 * m + k * (4 + idx_bytes) + 8 + (nnz * 8) / n
+        gather = nnz * k * (4 + idx_bytes)
+        extra = {"edges": nnz, "edges_per_s": nnz / (avg_launch_ms * 1e-3),
+                 "gather_bytes_per_launch": gather,
+                 "gather_gbs": gather / (avg_launch_ms * 1e-3) / 1e9}
+    algo_bytes = int(n * per_row)
     achieved = algo_bytes / (avg_launch_ms * 1e-3) / 1e9
     workload = workload_name(args)
     traffic = measured_traffic(workload)
@@ -326,6 +361,8 @@ def main():
         if args.op == "maxk_backward":
             g_np = grads[0].cpu().numpy()
             i_np = idxs[0].cpu().numpy().astype(np.int32)
+        if args.op == "spgemm":
+            sp_np = (feats[0][0].cpu().numpy(), feats[0][1].cpu().numpy().astype(np.int32))
         passes, t_cpu = 0, 0.0
         while t_cpu < args.cpu_seconds and passes < 100:
             t = time.perf_counter()
@@ -335,6 +372,8 @@ def main():
                 oracle.maxk_forward(x_np, k)
             elif args.op == "bucketed":
                 oracle.bucketed(x_np, k, args.buckets)
+            elif args.op == "spgemm":
+                oracle.spgemm(rp_np, ci_np, va_np, n, sp_np[0], sp_np[1], m)
             elif args.mode == "exact":
                 oracle.exact(x_np, k)
             else:
@@ -350,6 +389,8 @@ def main():
         "metric": (METRIC if args.op == "select" else
                    f"rows/sec and achieved HBM GB/s (% of peak), bucketed top-k "
                    f"N={n} M={m} k={k} buckets={args.buckets} fp32" if args.op == "bucketed" else
+                   f"rows/sec and achieved HBM GB/s (% of peak), MaxK-GNN aggregation "
+                   f"N={n} M={m} k={k} fp32" if args.op == "spgemm" else
                    f"rows/sec and achieved HBM GB/s (% of peak), MaxK "
                    f"{args.op.split('_')[1]} N={n} M={m} k={k} fp32"),
         "value": n / (ms_per_step * 1e-3),
@@ -378,6 +419,7 @@ def main():
     }
     if quality is not None:
         line["quality_vs_exact"] = quality
+    line.update(extra)
     print(json.dumps(line), flush=True)
 
 

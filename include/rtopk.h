@@ -181,6 +181,51 @@ rtopk_status_t rtopk_maxk_backward_u8(const float* grad_sp,
                                       int32_t M, int32_t k, float* grad_x,
                                       hipStream_t stream);
 
+/*
+ * MaxK-GNN forward aggregation (MaxK-GNN review, "How MaxK-GNN works": a
+ * row-wise product SpGEMM over the compressed features, each output row
+ * accumulated on chip and written once; abstract: CBSR feature fetching and
+ * a shared-memory accumulation buffer). Computes the dense
+ *   y[i*M + c] = sum over e in [row_ptr[i], row_ptr[i+1]) and t < k with
+ *                sp_index[col_idx[e]*k + t] == c of val[e] * sp_data[col_idx[e]*k + t]
+ * in single precision (fused multiply-adds in an unspecified order:
+ * the result differs from the exact sum by at most (d + 1) * 2^-24 times the
+ * sum of the terms' magnitudes, d the number of terms; rows cut between two
+ * work ranges are summed with atomics, so repeated calls may differ in the
+ * last bits).
+ *   row_ptr   device pointer to n_dst + 1 int64: the CSR row offsets of A,
+ *             nondecreasing, row_ptr[0] == 0, row_ptr[n_dst] == nnz.
+ *   col_idx   device pointer to nnz int32 source rows in [0, n_src).
+ *   val       device pointer to nnz floats: the edge weights.
+ *   n_dst     rows of A and of y (>= 0); n_src rows of the compressed
+ *             features (>= 1 when nnz > 0); nnz edges (>= 0).
+ *   sp_data, sp_index  the compressed features, [n_src, k] floats and
+ *             int32 (uint8 for the _u8 form) columns in [0, M), distinct
+ *             within a row, as written by rtopk_select_exact or
+ *             rtopk_maxk_forward (with repeated columns in a row the result
+ *             is unspecified).
+ *   M, k      feature width and survivors per row, 1 <= k <= M <= 8192.
+ *   y         device pointer to n_dst * M floats, written (every element).
+ * Edges whose column lies outside [0, n_src) and survivors whose column lies
+ * outside [0, M) contribute nothing. With row_ptr breaking its conditions
+ * the result is unspecified, but every access stays inside the arrays. Two
+ * kernels are enqueued on `stream` (rows cut between ranges are zeroed
+ * first). Errors as above, plus RTOPK_ERROR_INVALID_VALUE for nnz < 0,
+ * n_src < 0, or n_src == 0 with nnz > 0.
+ */
+rtopk_status_t rtopk_cbsr_spgemm(const int64_t* row_ptr, const int32_t* col_idx,
+                                 const float* val, int64_t n_dst, int64_t n_src,
+                                 int64_t nnz, const float* sp_data,
+                                 const int32_t* sp_index, int32_t M, int32_t k,
+                                 float* y, hipStream_t stream);
+
+/* As rtopk_cbsr_spgemm with one-byte survivor columns. Requires M <= 256. */
+rtopk_status_t rtopk_cbsr_spgemm_u8(const int64_t* row_ptr, const int32_t* col_idx,
+                                    const float* val, int64_t n_dst, int64_t n_src,
+                                    int64_t nnz, const float* sp_data,
+                                    const uint8_t* sp_index, int32_t M, int32_t k,
+                                    float* y, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* rtopk_status_string(rtopk_status_t status);
 

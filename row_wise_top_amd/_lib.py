@@ -44,12 +44,15 @@ def lib() -> ctypes.CDLL:
     l.rtopk_maxk_forward.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
     l.rtopk_maxk_forward_u8.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
     l.rtopk_maxk_backward.argtypes = [vp, vp, i64, i32, i32, vp, vp]
+    l.rtopk_cbsr_spgemm.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i32, i32, vp, vp]
+    l.rtopk_cbsr_spgemm_u8.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i32, i32, vp, vp]
     l.rtopk_maxk_backward_u8.argtypes = [vp, vp, i64, i32, i32, vp, vp]
     for f in (l.rtopk_select, l.rtopk_select_u8, l.rtopk_select_exact,
               l.rtopk_select_exact_u8, l.rtopk_select_bucketed,
               l.rtopk_select_bucketed_u8, l.rtopk_maxk_forward,
               l.rtopk_maxk_forward_u8, l.rtopk_maxk_backward,
-              l.rtopk_maxk_backward_u8):
+              l.rtopk_maxk_backward_u8, l.rtopk_cbsr_spgemm,
+              l.rtopk_cbsr_spgemm_u8):
         f.restype = ctypes.c_int
     l.rtopk_status_string.argtypes = [ctypes.c_int]
     l.rtopk_status_string.restype = ctypes.c_char_p
@@ -206,3 +209,37 @@ def rtopk_maxk_backward(grad_sp, sp_index, m: int, grad_x=None, stream=None):
               _stream(grad_sp, stream)),
            "rtopk_maxk_backward_u8" if u8 else "rtopk_maxk_backward")
     return grad_x
+
+
+def rtopk_cbsr_spgemm(row_ptr, col_idx, val, sp_data, sp_index, m: int, y=None,
+                      stream=None):
+    """MaxK-GNN aggregation y = A X: A in CSR (row_ptr int64 [n_dst + 1],
+    col_idx int32 [nnz], val float32 [nnz]), X as compressed rows (sp_data
+    float32 [n_src, k], sp_index int32 or uint8 [n_src, k], m columns).
+    Returns y, float32 [n_dst, m]."""
+    import torch
+    for t, dt, name in ((row_ptr, (torch.int64,), "row_ptr"), (col_idx, (torch.int32,), "col_idx"),
+                        (val, (torch.float32,), "val"), (sp_data, (torch.float32,), "sp_data"),
+                        (sp_index, (torch.int32, torch.uint8), "sp_index")):
+        if (not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype not in dt
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous GPU tensor of dtype {dt}")
+    if row_ptr.dim() != 1 or col_idx.dim() != 1 or val.shape != col_idx.shape:
+        raise ValueError("row_ptr, col_idx and val must be 1-D, col_idx and val of one length")
+    if sp_data.dim() != 2 or sp_index.shape != sp_data.shape:
+        raise ValueError("sp_data and sp_index must be [n_src, k] tensors of one shape")
+    n_dst = row_ptr.shape[0] - 1
+    n_src, k = sp_data.shape
+    nnz = col_idx.shape[0]
+    if y is None:
+        y = torch.empty((n_dst, m), dtype=torch.float32, device=sp_data.device)
+    if (y.device != sp_data.device or y.dtype != torch.float32 or not y.is_contiguous()
+            or tuple(y.shape) != (n_dst, m)):
+        raise ValueError(f"y must be a contiguous [{n_dst}, {m}] float32 tensor")
+    u8 = sp_index.dtype == torch.uint8
+    fn = lib().rtopk_cbsr_spgemm_u8 if u8 else lib().rtopk_cbsr_spgemm
+    _check(fn(row_ptr.data_ptr(), col_idx.data_ptr(), val.data_ptr(), n_dst, n_src, nnz,
+              sp_data.data_ptr(), sp_index.data_ptr(), m, k, y.data_ptr(),
+              _stream(sp_data, stream)),
+           "rtopk_cbsr_spgemm_u8" if u8 else "rtopk_cbsr_spgemm")
+    return y

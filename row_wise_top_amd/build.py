@@ -23,7 +23,8 @@ LIB = os.path.join(HERE, "librtopk.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["rtopk_api.hip", "rtopk_dispatch.hip", "rtopk_rows_a.hip",
            "rtopk_rows_b.hip", "rtopk_rows_c.hip", "rtopk_rows_d.hip",
-           "rtopk_rows_e.hip", "rtopk_rows_f.hip", "rtopk_maxk.hip"]
+           "rtopk_rows_e.hip", "rtopk_rows_f.hip", "rtopk_maxk.hip",
+           "rtopk_spgemm.hip"]
 ARCH = "gfx950"
 
 HIP_FLAGS = [

@@ -98,6 +98,27 @@ rtopk_status_t run_bucketed(const float* x, int64_t n, int32_t m, int32_t k,
   return err == hipSuccess ? RTOPK_SUCCESS : RTOPK_ERROR_LAUNCH;
 }
 
+rtopk_status_t run_spgemm(const int64_t* row_ptr, const int32_t* col,
+                          const float* val, int64_t n_dst, int64_t n_src,
+                          int64_t nnz, const float* sp_data, const void* sp_index,
+                          int32_t m, int32_t k, float* y, bool u8_index,
+                          hipStream_t stream) {
+  if (n_dst < 0 || n_src < 0 || nnz < 0 || m < 1 || k < 1 || k > m)
+    return RTOPK_ERROR_INVALID_VALUE;
+  if (nnz > 0 && n_src < 1) return RTOPK_ERROR_INVALID_VALUE;
+  if (m > rtopk::kMaxRowLength) return RTOPK_ERROR_NOT_SUPPORTED;
+  if (u8_index && m > 256) return RTOPK_ERROR_NOT_SUPPORTED;
+  if (n_dst > 0 && (row_ptr == nullptr || y == nullptr)) return RTOPK_ERROR_INVALID_VALUE;
+  if (nnz > 0 && (col == nullptr || val == nullptr || sp_data == nullptr ||
+                  sp_index == nullptr))
+    return RTOPK_ERROR_INVALID_VALUE;
+  if (n_dst == 0) return RTOPK_SUCCESS;
+  rtopk::SpgemmArgs a{row_ptr, col, val, n_dst, n_src, nnz, sp_data, sp_index,
+                      m, k, y, 0, 0, 0, 0, 0};
+  const hipError_t err = rtopk::launch_spgemm(a, u8_index, stream);
+  return err == hipSuccess ? RTOPK_SUCCESS : RTOPK_ERROR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -153,6 +174,24 @@ rtopk_status_t rtopk_maxk_forward_u8(const float* x, int64_t N, int32_t M,
                                      int32_t k, float* y, float* sp_data,
                                      uint8_t* sp_index, hipStream_t stream) {
   return run_maxk_forward(x, N, M, k, y, sp_data, sp_index, true, stream);
+}
+
+rtopk_status_t rtopk_cbsr_spgemm(const int64_t* row_ptr, const int32_t* col_idx,
+                                 const float* val, int64_t n_dst, int64_t n_src,
+                                 int64_t nnz, const float* sp_data,
+                                 const int32_t* sp_index, int32_t M, int32_t k,
+                                 float* y, hipStream_t stream) {
+  return run_spgemm(row_ptr, col_idx, val, n_dst, n_src, nnz, sp_data, sp_index,
+                    M, k, y, false, stream);
+}
+
+rtopk_status_t rtopk_cbsr_spgemm_u8(const int64_t* row_ptr, const int32_t* col_idx,
+                                    const float* val, int64_t n_dst, int64_t n_src,
+                                    int64_t nnz, const float* sp_data,
+                                    const uint8_t* sp_index, int32_t M, int32_t k,
+                                    float* y, hipStream_t stream) {
+  return run_spgemm(row_ptr, col_idx, val, n_dst, n_src, nnz, sp_data, sp_index,
+                    M, k, y, true, stream);
 }
 
 rtopk_status_t rtopk_maxk_backward(const float* grad_sp,

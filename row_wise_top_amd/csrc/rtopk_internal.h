@@ -96,6 +96,36 @@ struct ScatterArgs {
 hipError_t launch_scatter(const ScatterArgs& a, bool u8_index,
                           hipStream_t stream);
 
+// MaxK-GNN forward aggregation Y = A X (rtopk_spgemm.hip): A in CSR, X as
+// compressed rows (sp_data, sp_index: k survivors of m columns per row).
+struct SpgemmArgs {
+  const int64_t* row_ptr;  // [n_dst + 1]
+  const int32_t* col;      // [nnz], source rows
+  const float* val;        // [nnz]
+  int64_t n_dst;
+  int64_t n_src;           // >= 1
+  int64_t nnz;
+  const float* sp_data;    // [n_src, k]
+  const void* sp_index;    // [n_src, k] int32_t or uint8_t
+  int32_t m;
+  int32_t k;
+  float* y;                // [n_dst, m]
+  // Set by launch_spgemm.
+  int64_t chunk;           // edges per wave
+  int64_t waves;           // waves of the main kernel
+  int32_t m_pad;           // LDS floats per wave
+  int32_t waves_per_block; // 1 to kWavesPerBlock
+  int32_t slots;           // edges per step (accumulator rows per wave)
+};
+
+// Edges each wave of the aggregation takes.
+constexpr int64_t kEdgesPerWave = 256;
+
+// Enqueue the aggregation (a zeroing kernel for rows cut by a wave's range,
+// then the main kernel). Arguments validated (n_dst >= 0, n_src >= 1 when
+// nnz > 0, 1 <= k <= m <= kMaxRowLength).
+hipError_t launch_spgemm(SpgemmArgs a, bool u8_index, hipStream_t stream);
+
 // Enqueue the selection kernel for `a` on `stream`. Arguments are already
 // validated (1 <= k <= m <= kMaxRowLength, n > 0, u8 only with m <= 256).
 // Returns the HIP error of the launch.

@@ -1,0 +1,254 @@
+// MaxK-GNN forward aggregation on gfx950: Y = A X with A a CSR graph and X
+// given by its compressed MaxK rows (k survivors of M columns: sp_data,
+// sp_index). MaxK-GNN review, "How MaxK-GNN works": a row-wise product
+// SpGEMM that accumulates each output row on chip and writes it to global
+// memory once; the abstract names the compressed balanced layout for the
+// feature fetches and a shared-memory accumulation buffer.
+//
+// Work split. Power-law graphs have rows thousands of edges long, so rows
+// are not the unit of work: wave w takes edges [w*C, (w+1)*C) of the CSR
+// arrays (C = kEdgesPerWave) and every row that starts there, plus the part
+// of the row that was cut at its first edge. Each row (or part of a row) is
+// accumulated in the wave's own LDS rows (one lane per (edge, survivor)
+// pair, up to 4 edges per instruction, see accumulate), then flushed:
+//  * a row wholly inside the wave's range is stored once;
+//  * a row cut by a range boundary is added to Y with float atomics; such
+//    rows are zeroed first by a small kernel (one wave per boundary).
+// Every wave does about the same number of edges whatever the degree
+// distribution, and each complete row still reaches HBM exactly once.
+//
+// Inputs that break the preconditions (row_ptr not nondecreasing, indices
+// out of range) give an unspecified result but no out-of-bounds access:
+// every read is clamped into its array and out-of-range columns and
+// indices are skipped.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rtopk_internal.h"
+
+namespace rtopk {
+namespace spgemm_detail {
+
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ uint64_t ballot(bool p) {
+  return __builtin_amdgcn_ballot_w64(p);
+}
+
+// Largest i in [0, n] with row_ptr[i] <= p, by a 64-way search (each step
+// samples 64 positions, one per lane). row_ptr[0] <= p is assumed; with a
+// row_ptr that is not nondecreasing the result is some i in [0, n].
+__device__ int64_t last_row_at_or_before(const int64_t* __restrict__ row_ptr,
+                                         int64_t n, int64_t p, int lane) {
+  int64_t lo = 0, hi = n;
+  while (hi > lo) {
+    const int64_t step = (hi - lo + 63) / 64;
+    const int64_t q = lo + (lane + 1) * step;
+    const bool le = q <= hi && row_ptr[q <= hi ? q : hi] <= p;
+    const int cnt = __popcll(ballot(le));
+    const int64_t new_hi = lo + (cnt + 1) * step - 1;
+    lo = lo + cnt * step;
+    hi = new_hi < hi ? new_hi : hi;
+  }
+  return lo;
+}
+
+// Clamp a row_ptr entry into [0, nnz].
+__device__ __forceinline__ int64_t clamp_edge(int64_t e, int64_t nnz) {
+  return e < 0 ? 0 : (e > nnz ? nnz : e);
+}
+
+// Zero Y[i, :] for every row i cut by an interior range boundary
+// p = w * C (w >= 1): row_ptr[i] < p < row_ptr[i + 1].
+__global__ __launch_bounds__(kBlock) void zero_cut_rows(SpgemmArgs a) {
+  const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock +
+                    __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave) + 1;
+  const int64_t p = w * a.chunk;
+  if (p >= a.nnz) return;
+  const int64_t i = last_row_at_or_before(a.row_ptr, a.n_dst, p, lane);
+  if (i >= a.n_dst) return;
+  const int64_t start = a.row_ptr[i];
+  const int64_t end = a.row_ptr[i + 1];
+  if (!(start < p && p < end)) return;
+  const __amdgpu_buffer_rsrc_t ry =
+      __builtin_amdgcn_make_buffer_rsrc(a.y + i * a.m, 0, a.m * 4, kRsrcWord3);
+  for (int c = lane; c < a.m; c += kWave)
+    __builtin_amdgcn_raw_buffer_store_b32(0u, ry, c * 4, 0, 0);
+}
+
+// Accumulate edges [s0, s1) of a row into the wave's LDS accumulators. The
+// edges' source rows and weights come from the wave's LDS copy of its edge
+// range (ecol / eval, indexed from the range's first edge e0), so the only
+// global loads in the loop are the features, issued for U steps at a time.
+//
+// Lane roles: a step takes P edges (P = min(4, 64 / k) for k <= 64, else 1);
+// lane l serves edge slot l / k and survivor l % k (lanes past P*k idle;
+// for k > 64 each edge takes ceil(k / 64) passes). Each edge slot adds into
+// its own accumulator row (accp), with a plain read, fma and write: the
+// survivors of one edge have distinct columns and the slots never share a
+// row, so no two lanes of an instruction touch one word, and the LDS
+// pipeline applies one wave's instructions in order. (LDS float atomics
+// would serialise about one lane per clock.)
+template <typename IdxT>
+__device__ __forceinline__ void accumulate(const SpgemmArgs& a, int64_t e0,
+                                           int64_t s0, int64_t s1, float* accp,
+                                           const int* ecol, const float* eval,
+                                           int lane_edge, int lane_t, int P) {
+  const IdxT* sidx = static_cast<const IdxT*>(a.sp_index);
+  const int k = a.k;
+  // Idle lanes (lane_edge < 0) address the step's first edge and add nothing.
+  const int addr_edge = lane_edge < 0 ? 0 : lane_edge;
+  constexpr int U = 8;  // steps whose feature loads are issued together
+  for (int64_t b0 = s0; b0 < s1; b0 += static_cast<int64_t>(U) * P) {
+    for (int t0 = lane_t; t0 < k; t0 += kWave) {
+      float xv[U], w[U];
+      int xc[U];
+      bool ok[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t e = b0 + static_cast<int64_t>(u) * P + addr_edge;
+        const int64_t ec = e < s1 ? e : s1 - 1;  // stays inside the staged range
+        const int col = ecol[ec - e0];
+        w[u] = eval[ec - e0];
+        const bool live = lane_edge >= 0 && e < s1 &&
+                          static_cast<uint64_t>(static_cast<int64_t>(col)) <
+                              static_cast<uint64_t>(a.n_src);
+        const int64_t j = live ? col : 0;
+        xv[u] = a.sp_data[j * k + t0];
+        xc[u] = static_cast<int>(sidx[j * k + t0]);
+        ok[u] = live;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (ok[u] && static_cast<uint32_t>(xc[u]) < static_cast<uint32_t>(a.m))
+          accp[xc[u]] = fmaf(w[u], xv[u], accp[xc[u]]);
+      }
+      if (k <= kWave) break;  // one pass covers the survivors
+    }
+  }
+}
+
+// Store (or, for a cut row, add) the sum of the wave's P accumulator rows to
+// Y[i, :], then zero them.
+__device__ __forceinline__ void flush(const SpgemmArgs& a, int64_t i, float* acc,
+                                      int P, int lane, bool cut) {
+  __builtin_amdgcn_wave_barrier();
+  const __amdgpu_buffer_rsrc_t ry =
+      __builtin_amdgcn_make_buffer_rsrc(a.y + i * a.m, 0, a.m * 4, kRsrcWord3);
+  for (int c = lane; c < a.m; c += kWave) {
+    float v = acc[c];
+    acc[c] = 0.0f;
+    for (int p = 1; p < P; ++p) {
+      v += acc[p * a.m_pad + c];
+      acc[p * a.m_pad + c] = 0.0f;
+    }
+    if (cut)
+      unsafeAtomicAdd(a.y + i * a.m + c, v);  // hardware float atomic
+    else
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ry, c * 4, 0, 0);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Blocks of a.waves_per_block waves (fewer for long rows, so that a block's
+// LDS rows stay within 64 KB).
+template <typename IdxT>
+__global__ __launch_bounds__(kBlock) void spgemm_rows(SpgemmArgs a) {
+  extern __shared__ float lds[];
+  const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+  const int wave_in_block =
+      __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  // Per wave: P accumulator rows (m_pad floats each), then the staged edge
+  // range (kEdgesPerWave source rows, kEdgesPerWave weights).
+  const int P = a.slots;
+  float* acc = lds + static_cast<int64_t>(wave_in_block) * (P * a.m_pad + 2 * kEdgesPerWave);
+  int* ecol = reinterpret_cast<int*>(acc + P * a.m_pad);
+  float* eval = acc + P * a.m_pad + kEdgesPerWave;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * a.waves_per_block + wave_in_block;
+  if (w >= a.waves) return;
+  const int64_t nnz = a.nnz;
+  const int64_t e0 = w * a.chunk;
+  const int64_t e1 = e0 + a.chunk < nnz ? e0 + a.chunk : nnz;
+  const bool last = w == a.waves - 1;
+  // Stage the range's edges (coalesced; positions past e1 re-read e1 - 1).
+  for (int j = lane; j < kEdgesPerWave; j += kWave) {
+    const int64_t e = e0 + j < e1 ? e0 + j : e1 - 1;
+    ecol[j] = e >= 0 ? a.col[e] : 0;
+    eval[j] = e >= 0 ? a.val[e] : 0.0f;
+  }
+  // LDS operations of one wave complete in issue order; the barrier keeps
+  // the compiler from moving the reads below above these writes.
+  __builtin_amdgcn_wave_barrier();
+  // Lane roles: edge slot within a step and survivor index.
+  const int k = a.k;
+  const int lane_edge = k <= kWave ? (lane < P * k ? lane / k : -1) : 0;
+  const int lane_t = k <= kWave ? lane % k : lane;
+  float* accp = acc + (lane_edge > 0 ? lane_edge : 0) * a.m_pad;
+  for (int c = lane; c < P * a.m_pad; c += kWave) acc[c] = 0.0f;
+  __builtin_amdgcn_wave_barrier();
+  // The row cut at e0 (started in an earlier range): add its part.
+  int64_t i = 0;
+  if (e0 > 0) {
+    const int64_t ic = last_row_at_or_before(a.row_ptr, a.n_dst, e0, lane);
+    if (ic < a.n_dst && clamp_edge(a.row_ptr[ic], nnz) < e0) {
+      const int64_t end = clamp_edge(a.row_ptr[ic + 1], nnz);
+      accumulate<IdxT>(a, e0, e0, end < e1 ? end : e1, accp, ecol, eval, lane_edge,
+                       lane_t, P);
+      flush(a, ic, acc, P, lane, true);
+      i = ic + 1;
+    } else {
+      // First row that starts at or after e0.
+      i = last_row_at_or_before(a.row_ptr, a.n_dst, e0 - 1, lane) + 1;
+    }
+  }
+  // Rows that start in [e0, e1) (the last wave also takes those starting at
+  // nnz, i.e. trailing empty rows).
+  for (; i < a.n_dst; ++i) {
+    const int64_t start = clamp_edge(a.row_ptr[i], nnz);
+    if (start >= e1 && !(last && start == nnz)) break;
+    if (start < e0) continue;  // only with a row_ptr that decreases
+    const int64_t end = clamp_edge(a.row_ptr[i + 1], nnz);
+    const bool cut = end > e1;
+    accumulate<IdxT>(a, e0, start, cut ? e1 : end, accp, ecol, eval, lane_edge,
+                     lane_t, P);
+    flush(a, i, acc, P, lane, cut);
+  }
+}
+
+}  // namespace spgemm_detail
+
+hipError_t launch_spgemm(SpgemmArgs a, bool u8_index, hipStream_t stream) {
+  using namespace spgemm_detail;
+  a.chunk = kEdgesPerWave;
+  a.waves = a.nnz > 0 ? (a.nnz + a.chunk - 1) / a.chunk : 1;
+  a.m_pad = (a.m + 3) & ~3;
+  a.slots = a.k <= kWave ? (kWave / a.k < 4 ? kWave / a.k : 4) : 1;
+  const int per_wave_bytes =
+      (a.slots * a.m_pad + 2 * static_cast<int>(kEdgesPerWave)) * static_cast<int>(sizeof(float));
+  int wpb = 65536 / per_wave_bytes;
+  a.waves_per_block = wpb < 1 ? 1 : (wpb > kWavesPerBlock ? kWavesPerBlock : wpb);
+  const int64_t blocks = (a.waves + a.waves_per_block - 1) / a.waves_per_block;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  // Rows cut by a range boundary start at zero.
+  const int64_t boundaries = a.waves - 1;
+  if (boundaries > 0) {
+    const int64_t zb = (boundaries + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL(zero_cut_rows, dim3(static_cast<uint32_t>(zb)), dim3(kBlock), 0,
+                       stream, a);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  const size_t lds = static_cast<size_t>(a.waves_per_block) * per_wave_bytes;
+  const dim3 block(kWave * a.waves_per_block);
+  if (u8_index)
+    hipLaunchKernelGGL(spgemm_rows<uint8_t>, dim3(static_cast<uint32_t>(blocks)),
+                       block, lds, stream, a);
+  else
+    hipLaunchKernelGGL(spgemm_rows<int32_t>, dim3(static_cast<uint32_t>(blocks)),
+                       block, lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace rtopk

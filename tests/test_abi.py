@@ -25,7 +25,8 @@ def test_header_declares_expected_entry_points():
         "rtopk_select", "rtopk_select_exact", "rtopk_select_u8",
         "rtopk_select_exact_u8", "rtopk_select_bucketed", "rtopk_select_bucketed_u8",
         "rtopk_maxk_forward", "rtopk_maxk_forward_u8",
-        "rtopk_maxk_backward", "rtopk_maxk_backward_u8", "rtopk_status_string"])
+        "rtopk_maxk_backward", "rtopk_maxk_backward_u8", "rtopk_cbsr_spgemm",
+        "rtopk_cbsr_spgemm_u8", "rtopk_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -193,3 +194,39 @@ def test_bucketed_null_pointers(fn, which):
     ptrs = [FAKE, FAKE, FAKE]
     ptrs[which] = None
     assert call(fn, ptrs[0], 4, 16, 4, 2, ptrs[1], ptrs[2], None) == 1
+
+
+SPGEMM = ["rtopk_cbsr_spgemm", "rtopk_cbsr_spgemm_u8"]
+
+
+@pytest.mark.parametrize("fn", SPGEMM)
+def test_spgemm_no_rows_is_a_noop(fn):
+    assert call(fn, None, None, None, 0, 0, 0, None, None, 16, 4, None, None) == 0
+
+
+@pytest.mark.parametrize("fn", SPGEMM)
+@pytest.mark.parametrize("n_dst,n_src,nnz,m,k,code", [
+    (-1, 4, 4, 16, 4, 1),     # n_dst < 0
+    (4, -1, 4, 16, 4, 1),     # n_src < 0
+    (4, 4, -1, 16, 4, 1),     # nnz < 0
+    (4, 0, 4, 16, 4, 1),      # edges but no source rows
+    (4, 4, 4, 16, 17, 1),     # k > M
+    (4, 4, 4, 0, 1, 1),       # M < 1
+    (4, 4, 4, 8193, 4, 2),    # M above the maximum
+])
+def test_spgemm_argument_errors(fn, n_dst, n_src, nnz, m, k, code):
+    assert call(fn, FAKE, FAKE, FAKE, n_dst, n_src, nnz, FAKE, FAKE, m, k, FAKE, None) == code
+
+
+def test_spgemm_u8_requires_short_rows():
+    assert call("rtopk_cbsr_spgemm_u8", FAKE, FAKE, FAKE, 4, 4, 4, FAKE, FAKE, 257, 4,
+                FAKE, None) == 2
+
+
+@pytest.mark.parametrize("fn", SPGEMM)
+@pytest.mark.parametrize("which", [0, 1, 2, 3, 4, 5])
+def test_spgemm_null_pointers(fn, which):
+    ptrs = [FAKE] * 6
+    ptrs[which] = None
+    assert call(fn, ptrs[0], ptrs[1], ptrs[2], 4, 4, 4, ptrs[3], ptrs[4], 16, 4,
+                ptrs[5], None) == 1
