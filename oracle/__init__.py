@@ -15,6 +15,8 @@ Both return the survivors of each row in ascending index order.
 Increased Parallelism"): exact top-(k/b) of each of b contiguous buckets.
 ``spgemm`` is MaxK-GNN's forward aggregation Y = A X (CSR graph A, X given
 by its compressed MaxK rows), summed in double and rounded once.
+``sspmm`` is its backward to the compressed features: (A^T dY) sampled at
+the survivors' columns.
 ``maxk_forward`` / ``maxk_backward`` are the MaxK nonlinearity of the MaxK-GNN
 review ("How MaxK-GNN works"): the dense [N, M] output that keeps each row's
 exact top-k and zeroes the rest, and the gradient that flows back only to the
@@ -78,6 +80,10 @@ def _load():
                                   f32p, i32p, ctypes.c_int32, ctypes.c_int32,
                                   f32p, f32p]
     lib.oracle_spgemm.restype = ctypes.c_int
+    lib.oracle_sspmm.argtypes = [i64p, i32p, f32p, ctypes.c_int64, ctypes.c_int64,
+                                 f32p, i32p, ctypes.c_int32, ctypes.c_int32,
+                                 f32p, f32p]
+    lib.oracle_sspmm.restype = ctypes.c_int
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
     _lib = lib
@@ -197,6 +203,29 @@ def spgemm(row_ptr, col_idx, val, n_src: int, sp_data, sp_index, m: int,
     if rc != 0:
         raise ValueError("oracle_spgemm: invalid arguments")
     return (y, ab) if return_absum else y
+
+
+def sspmm(row_ptr, col_idx, val, dy, sp_index, return_absum: bool = False):
+    """grad_sp [n_src, k] = (A^T dy) at the survivors' columns sp_index."""
+    rp = np.ascontiguousarray(row_ptr, dtype=np.int64)
+    ci = np.ascontiguousarray(col_idx, dtype=np.int32)
+    va = np.ascontiguousarray(val, dtype=np.float32)
+    g = np.ascontiguousarray(dy, dtype=np.float32)
+    si = np.ascontiguousarray(sp_index, dtype=np.int32)
+    n_dst = rp.shape[0] - 1
+    n_src, k = si.shape
+    if g.ndim != 2 or g.shape[0] != n_dst or ci.shape != va.shape:
+        raise ValueError("inconsistent shapes")
+    m = g.shape[1]
+    out = np.empty((n_src, k), dtype=np.float32)
+    ab = np.empty((n_src, k), dtype=np.float32) if return_absum else None
+    rc = _load().oracle_sspmm(
+        rp.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ip(ci), _fp(va),
+        n_dst, n_src, _fp(g), _ip(si), m, k, _fp(out),
+        _fp(ab) if ab is not None else None)
+    if rc != 0:
+        raise ValueError("oracle_sspmm: invalid arguments")
+    return (out, ab) if return_absum else out
 
 
 def threads() -> int:

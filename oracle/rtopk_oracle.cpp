@@ -41,6 +41,14 @@
 //                     of val[e] * X[col[e], :]. Plain definition, summed in
 //                     double and rounded once.
 //
+//   oracle_sspmm   -- the backward of that aggregation with respect to the
+//                     compressed features (review page: the backward reuses
+//                     the forward's sparsity pattern and samples exactly the
+//                     sp_index positions): grad_sp[j, t] = sum over edges e
+//                     with col[e] == j, e in row i, of val[e] * dY[i,
+//                     sp_index[j, t]], i.e. (A^T dY) sampled at the
+//                     survivors. Summed in double, rounded once.
+//
 //   oracle_capped  -- the threshold search of the RTop-K summary page, section
 //                     "Approach": bisection over the row's value range until a
 //                     threshold selects k elements, an optional cap on the
@@ -258,6 +266,38 @@ int oracle_spgemm(const int64_t* row_ptr, const int32_t* col, const float* val,
       y[i * M + c] = static_cast<float>(acc[c]);
       if (absum) absum[i * M + c] = static_cast<float>(mag[c] * (1.0 + 1e-6));
     }
+  }
+  return 0;
+}
+
+// grad_sp [n_src, k] = (A^T dy) at (j, sp_index[j, t]); dy is [n_dst, M].
+// absum (optional, [n_src, k]) receives the sum of |terms|, rounded up.
+// Edges with a column outside [0, n_src) and survivors outside [0, M)
+// contribute nothing. Returns 0, or 1 on invalid arguments.
+int oracle_sspmm(const int64_t* row_ptr, const int32_t* col, const float* val,
+                 int64_t n_dst, int64_t n_src, const float* dy,
+                 const int32_t* sp_index, int32_t M, int32_t k, float* grad_sp,
+                 float* absum) {
+  if (n_dst < 0 || n_src < 0 || M < 1 || k < 1) return 1;
+  std::vector<double> acc(static_cast<size_t>(n_src) * k, 0.0);
+  std::vector<double> mag(static_cast<size_t>(n_src) * k, 0.0);
+  // Serial over edges: the scatter into grad rows would race in parallel.
+  for (int64_t i = 0; i < n_dst; ++i) {
+    for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+      const int64_t j = col[e];
+      if (j < 0 || j >= n_src) continue;
+      for (int t = 0; t < k; ++t) {
+        const int32_t c = sp_index[j * k + t];
+        if (c < 0 || c >= M) continue;
+        const double term = static_cast<double>(val[e]) * static_cast<double>(dy[i * M + c]);
+        acc[j * k + t] += term;
+        mag[j * k + t] += term < 0 ? -term : term;
+      }
+    }
+  }
+  for (size_t q = 0; q < acc.size(); ++q) {
+    grad_sp[q] = static_cast<float>(acc[q]);
+    if (absum) absum[q] = static_cast<float>(mag[q] * (1.0 + 1e-6));
   }
   return 0;
 }
