@@ -112,8 +112,8 @@ def workload_name(args) -> str:
     if args.op == "bucketed":
         return (f"bucketed {args.inputs} N={args.rows} M={args.m} k={args.k} "
                 f"buckets={args.buckets} idx={args.index}")
-    if args.op == "spgemm":
-        return (f"spgemm power-law graph N={args.rows} mean_degree={args.degree:g} "
+    if args.op in ("spgemm", "sspmm"):
+        return (f"{args.op} power-law graph N={args.rows} mean_degree={args.degree:g} "
                 f"M={args.m} k={args.k} idx={args.index}")
     return (f"{args.inputs} N={args.rows} M={args.m} k={args.k} {args.mode}"
             + ("" if args.mode == "exact" else f" max_iter={args.max_iter} eps={args.eps}")
@@ -123,14 +123,14 @@ def workload_name(args) -> str:
 # Name fragment of the kernel each op launches (for the counter records).
 OP_KERNEL = {"select": "rows_in_registers", "maxk_forward": "rows_in_registers",
              "maxk_backward": "scatter_rows", "bucketed": "rows_in_registers",
-             "spgemm": "spgemm_rows"}
+             "spgemm": "spgemm_rows", "sspmm": "sspmm_rows"}
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--op", choices=["select", "maxk_forward", "maxk_backward", "bucketed",
-                                    "spgemm"],
+                                    "spgemm", "sspmm"],
                    default="select",
                    help="select: row-wise top-k (the headline); maxk_forward: "
                         "the MaxK nonlinearity (dense output plus the compressed "
@@ -225,9 +225,10 @@ def main():
         def step(i):
             rt.rtopk_maxk_backward(grads[i % nbuf], idxs[i % nbuf], m,
                                    grad_x=outs[i % nout])
-    elif args.op == "spgemm":
+    elif args.op in ("spgemm", "sspmm"):
         # A power-law graph over the same rows; features: the exact top-k of
-        # each rotated buffer (from the library's selection). Outputs rotate.
+        # each rotated buffer (from the library's selection). Outputs rotate;
+        # for the backward the rotated inputs are dense gradients dY.
         sel = rt.rtopk_select_exact_u8 if u8 else rt.rtopk_select_exact
         feats = [sel(xb, k) for xb in xs]
         del xs
@@ -239,9 +240,19 @@ def main():
         nout = max(1, -(-768 * 2**20 // (n * m * 4)))
         outs = [torch.empty((n, m), dtype=torch.float32, device=dev) for _ in range(nout)]
 
-        def step(i):
-            fv, fi = feats[i % nbuf]
-            rt.rtopk_cbsr_spgemm(rp_t, ci_t, va_t, fv, fi, m, y=outs[i % nout])
+        if args.op == "spgemm":
+            def step(i):
+                fv, fi = feats[i % nbuf]
+                rt.rtopk_cbsr_spgemm(rp_t, ci_t, va_t, fv, fi, m, y=outs[i % nout])
+        else:
+            dys = outs
+            for b, t in enumerate(dys):
+                t.copy_(torch.from_numpy(workloads.normal(n, m, 90 + b)))
+            gs = [torch.empty((n, k), dtype=torch.float32, device=dev) for _ in range(nbuf)]
+
+            def step(i):
+                rt.rtopk_cbsr_sspmm(rp_t, ci_t, va_t, dys[i % nout], feats[i % nbuf][1],
+                                    grad_sp=gs[i % nbuf])
     elif args.op == "bucketed":
         def step(i):
             rt.rtopk_select_bucketed(xs[i % nbuf], k, args.buckets, out_val=out_v,
@@ -329,12 +340,16 @@ def main():
     # maxk_forward: M floats in, M floats and k entries out.
     per_row = 4 * m + k * (4 + idx_bytes) + (4 * m if args.op == "maxk_forward" else 0)
     extra = {}
-    if args.op == "spgemm":
+    if args.op in ("spgemm", "sspmm"):
         # Bytes that must cross HBM at least once per launch: the CSR arrays,
-        # each feature row once, each output row once. The per-edge gathers
-        # of neighbour rows (nnz * k * (4 + b)) are served mostly by the
-        # last-level cache and reported separately.
+        # each compressed row once, each dense row once (forward: output;
+        # backward: the input dY, plus the gradient written, k floats per
+        # row). The per-edge gathers of neighbour rows (nnz * k * (4 + b);
+        # backward: index rows plus atomics) are served mostly by the caches
+        # and reported separately.
         per_row = 4 * m + k * (4 + idx_bytes) + 8 + (nnz * 8) / n
+        if args.op == "sspmm":
+            per_row = 4 * m + k * (idx_bytes + 4) + 8 + (nnz * 8) / n
         gather = nnz * k * (4 + idx_bytes)
         extra = {"edges": nnz, "edges_per_s": nnz / (avg_launch_ms * 1e-3),
                  "gather_bytes_per_launch": gather,
@@ -361,8 +376,10 @@ def main():
         if args.op == "maxk_backward":
             g_np = grads[0].cpu().numpy()
             i_np = idxs[0].cpu().numpy().astype(np.int32)
-        if args.op == "spgemm":
+        if args.op in ("spgemm", "sspmm"):
             sp_np = (feats[0][0].cpu().numpy(), feats[0][1].cpu().numpy().astype(np.int32))
+        if args.op == "sspmm":
+            dy_np = dys[0].cpu().numpy()
         passes, t_cpu = 0, 0.0
         while t_cpu < args.cpu_seconds and passes < 100:
             t = time.perf_counter()
@@ -374,6 +391,8 @@ def main():
                 oracle.bucketed(x_np, k, args.buckets)
             elif args.op == "spgemm":
                 oracle.spgemm(rp_np, ci_np, va_np, n, sp_np[0], sp_np[1], m)
+            elif args.op == "sspmm":
+                oracle.sspmm(rp_np, ci_np, va_np, dy_np, sp_np[1])
             elif args.mode == "exact":
                 oracle.exact(x_np, k)
             else:
@@ -391,6 +410,8 @@ def main():
                    f"N={n} M={m} k={k} buckets={args.buckets} fp32" if args.op == "bucketed" else
                    f"rows/sec and achieved HBM GB/s (% of peak), MaxK-GNN aggregation "
                    f"N={n} M={m} k={k} fp32" if args.op == "spgemm" else
+                   f"rows/sec and achieved HBM GB/s (% of peak), MaxK-GNN aggregation backward "
+                   f"(SSpMM) N={n} M={m} k={k} fp32" if args.op == "sspmm" else
                    f"rows/sec and achieved HBM GB/s (% of peak), MaxK "
                    f"{args.op.split('_')[1]} N={n} M={m} k={k} fp32"),
         "value": n / (ms_per_step * 1e-3),

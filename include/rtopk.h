@@ -226,6 +226,43 @@ rtopk_status_t rtopk_cbsr_spgemm_u8(const int64_t* row_ptr, const int32_t* col_i
                                     const uint8_t* sp_index, int32_t M, int32_t k,
                                     float* y, hipStream_t stream);
 
+/*
+ * Backward of rtopk_cbsr_spgemm with respect to the compressed features
+ * (MaxK-GNN review, "How MaxK-GNN works": the backward samples exactly the
+ * sp_index positions, reusing the forward's sparsity pattern, with an
+ * outer-product dataflow and dense-row prefetching). Given the gradient dy
+ * of y, computes
+ *   grad_sp[j*k + t] = sum over edges e = (i -> j), i.e. e in
+ *                      [row_ptr[i], row_ptr[i+1]) with col_idx[e] == j, of
+ *                      val[e] * dy[i*M + sp_index[j*k + t]]
+ * (A^T dy sampled at the survivors), in single precision with float
+ * atomics: the order of the sums is unspecified and repeated calls may
+ * differ in the last bits (bound as for rtopk_cbsr_spgemm, d the number of
+ * edges into j).
+ *   row_ptr, col_idx, val, n_dst, n_src, nnz  the same CSR of A as the
+ *             forward (no transpose needed).
+ *   dy        device pointer to n_dst * M floats, read.
+ *   sp_index  device pointer to n_src * k int32 (uint8 for the _u8 form)
+ *             columns in [0, M), read.
+ *   grad_sp   device pointer to n_src * k floats, written (every element;
+ *             survivors with no edge get +0.0).
+ * Edges whose column lies outside [0, n_src) and survivors outside [0, M)
+ * contribute nothing. Two kernels are enqueued on `stream`. Errors as for
+ * rtopk_cbsr_spgemm (grad_sp may not be NULL when n_src > 0).
+ */
+rtopk_status_t rtopk_cbsr_sspmm(const int64_t* row_ptr, const int32_t* col_idx,
+                                const float* val, int64_t n_dst, int64_t n_src,
+                                int64_t nnz, const float* dy,
+                                const int32_t* sp_index, int32_t M, int32_t k,
+                                float* grad_sp, hipStream_t stream);
+
+/* As rtopk_cbsr_sspmm with one-byte survivor columns. Requires M <= 256. */
+rtopk_status_t rtopk_cbsr_sspmm_u8(const int64_t* row_ptr, const int32_t* col_idx,
+                                   const float* val, int64_t n_dst, int64_t n_src,
+                                   int64_t nnz, const float* dy,
+                                   const uint8_t* sp_index, int32_t M, int32_t k,
+                                   float* grad_sp, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* rtopk_status_string(rtopk_status_t status);
 

@@ -9,7 +9,8 @@ include/rtopk.h (librtopk.so); this package is a thin binding over it.
 
 from __future__ import annotations
 
-from ._lib import (RTOPK_MAX_ROW_LENGTH, lib, rtopk_cbsr_spgemm, rtopk_maxk_backward,
+from ._lib import (RTOPK_MAX_ROW_LENGTH, lib, rtopk_cbsr_spgemm, rtopk_cbsr_sspmm,
+                   rtopk_maxk_backward,
                    rtopk_maxk_forward, rtopk_select, rtopk_select_bucketed,
                    rtopk_select_exact, rtopk_select_exact_u8, rtopk_select_u8,
                    rtopk_status_string)
@@ -17,7 +18,7 @@ from ._lib import (RTOPK_MAX_ROW_LENGTH, lib, rtopk_cbsr_spgemm, rtopk_maxk_back
 __all__ = ["select", "lib", "rtopk_select", "rtopk_select_exact",
            "rtopk_select_u8", "rtopk_select_exact_u8", "rtopk_select_bucketed",
            "rtopk_maxk_forward",
-           "rtopk_maxk_backward", "rtopk_cbsr_spgemm",
+           "rtopk_maxk_backward", "rtopk_cbsr_spgemm", "rtopk_cbsr_sspmm",
            "rtopk_status_string", "RTOPK_MAX_ROW_LENGTH"]
 
 

@@ -46,13 +46,15 @@ def lib() -> ctypes.CDLL:
     l.rtopk_maxk_backward.argtypes = [vp, vp, i64, i32, i32, vp, vp]
     l.rtopk_cbsr_spgemm.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i32, i32, vp, vp]
     l.rtopk_cbsr_spgemm_u8.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i32, i32, vp, vp]
+    l.rtopk_cbsr_sspmm.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i32, i32, vp, vp]
+    l.rtopk_cbsr_sspmm_u8.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i32, i32, vp, vp]
     l.rtopk_maxk_backward_u8.argtypes = [vp, vp, i64, i32, i32, vp, vp]
     for f in (l.rtopk_select, l.rtopk_select_u8, l.rtopk_select_exact,
               l.rtopk_select_exact_u8, l.rtopk_select_bucketed,
               l.rtopk_select_bucketed_u8, l.rtopk_maxk_forward,
               l.rtopk_maxk_forward_u8, l.rtopk_maxk_backward,
               l.rtopk_maxk_backward_u8, l.rtopk_cbsr_spgemm,
-              l.rtopk_cbsr_spgemm_u8):
+              l.rtopk_cbsr_spgemm_u8, l.rtopk_cbsr_sspmm, l.rtopk_cbsr_sspmm_u8):
         f.restype = ctypes.c_int
     l.rtopk_status_string.argtypes = [ctypes.c_int]
     l.rtopk_status_string.restype = ctypes.c_char_p
@@ -243,3 +245,35 @@ def rtopk_cbsr_spgemm(row_ptr, col_idx, val, sp_data, sp_index, m: int, y=None,
               _stream(sp_data, stream)),
            "rtopk_cbsr_spgemm_u8" if u8 else "rtopk_cbsr_spgemm")
     return y
+
+
+def rtopk_cbsr_sspmm(row_ptr, col_idx, val, dy, sp_index, grad_sp=None, stream=None):
+    """Backward of rtopk_cbsr_spgemm to the compressed features: grad_sp
+    [n_src, k] = (A^T dy) at the survivors' columns sp_index (int32 or uint8,
+    [n_src, k]); dy is float32 [n_dst, M]."""
+    import torch
+    for t, dt, name in ((row_ptr, (torch.int64,), "row_ptr"), (col_idx, (torch.int32,), "col_idx"),
+                        (val, (torch.float32,), "val"), (dy, (torch.float32,), "dy"),
+                        (sp_index, (torch.int32, torch.uint8), "sp_index")):
+        if (not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype not in dt
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous GPU tensor of dtype {dt}")
+    if row_ptr.dim() != 1 or col_idx.dim() != 1 or val.shape != col_idx.shape:
+        raise ValueError("row_ptr, col_idx and val must be 1-D, col_idx and val of one length")
+    n_dst = row_ptr.shape[0] - 1
+    if dy.dim() != 2 or dy.shape[0] != n_dst or sp_index.dim() != 2:
+        raise ValueError("dy must be [n_dst, M] and sp_index [n_src, k]")
+    m = dy.shape[1]
+    n_src, k = sp_index.shape
+    if grad_sp is None:
+        grad_sp = torch.empty((n_src, k), dtype=torch.float32, device=dy.device)
+    if (grad_sp.device != dy.device or grad_sp.dtype != torch.float32
+            or not grad_sp.is_contiguous() or tuple(grad_sp.shape) != (n_src, k)):
+        raise ValueError(f"grad_sp must be a contiguous [{n_src}, {k}] float32 tensor")
+    u8 = sp_index.dtype == torch.uint8
+    fn = lib().rtopk_cbsr_sspmm_u8 if u8 else lib().rtopk_cbsr_sspmm
+    _check(fn(row_ptr.data_ptr(), col_idx.data_ptr(), val.data_ptr(), n_dst, n_src,
+              col_idx.shape[0], dy.data_ptr(), sp_index.data_ptr(), m, k,
+              grad_sp.data_ptr(), _stream(dy, stream)),
+           "rtopk_cbsr_sspmm_u8" if u8 else "rtopk_cbsr_sspmm")
+    return grad_sp

@@ -119,6 +119,27 @@ rtopk_status_t run_spgemm(const int64_t* row_ptr, const int32_t* col,
   return err == hipSuccess ? RTOPK_SUCCESS : RTOPK_ERROR_LAUNCH;
 }
 
+rtopk_status_t run_sspmm(const int64_t* row_ptr, const int32_t* col,
+                         const float* val, int64_t n_dst, int64_t n_src,
+                         int64_t nnz, const float* dy, const void* sp_index,
+                         int32_t m, int32_t k, float* grad_sp, bool u8_index,
+                         hipStream_t stream) {
+  if (n_dst < 0 || n_src < 0 || nnz < 0 || m < 1 || k < 1 || k > m)
+    return RTOPK_ERROR_INVALID_VALUE;
+  if (nnz > 0 && n_src < 1) return RTOPK_ERROR_INVALID_VALUE;
+  if (m > rtopk::kMaxRowLength) return RTOPK_ERROR_NOT_SUPPORTED;
+  if (u8_index && m > 256) return RTOPK_ERROR_NOT_SUPPORTED;
+  if (n_src > 0 && grad_sp == nullptr) return RTOPK_ERROR_INVALID_VALUE;
+  if (nnz > 0 && (row_ptr == nullptr || col == nullptr || val == nullptr ||
+                  dy == nullptr || sp_index == nullptr))
+    return RTOPK_ERROR_INVALID_VALUE;
+  if (n_src == 0) return RTOPK_SUCCESS;
+  rtopk::SpgemmArgs a{row_ptr, col, val, n_dst, n_src, nnz, dy, sp_index,
+                      m, k, grad_sp, 0, 0, 0, 0, 0};
+  const hipError_t err = rtopk::launch_sspmm(a, u8_index, stream);
+  return err == hipSuccess ? RTOPK_SUCCESS : RTOPK_ERROR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -192,6 +213,24 @@ rtopk_status_t rtopk_cbsr_spgemm_u8(const int64_t* row_ptr, const int32_t* col_i
                                     float* y, hipStream_t stream) {
   return run_spgemm(row_ptr, col_idx, val, n_dst, n_src, nnz, sp_data, sp_index,
                     M, k, y, true, stream);
+}
+
+rtopk_status_t rtopk_cbsr_sspmm(const int64_t* row_ptr, const int32_t* col_idx,
+                                const float* val, int64_t n_dst, int64_t n_src,
+                                int64_t nnz, const float* dy,
+                                const int32_t* sp_index, int32_t M, int32_t k,
+                                float* grad_sp, hipStream_t stream) {
+  return run_sspmm(row_ptr, col_idx, val, n_dst, n_src, nnz, dy, sp_index, M, k,
+                   grad_sp, false, stream);
+}
+
+rtopk_status_t rtopk_cbsr_sspmm_u8(const int64_t* row_ptr, const int32_t* col_idx,
+                                   const float* val, int64_t n_dst, int64_t n_src,
+                                   int64_t nnz, const float* dy,
+                                   const uint8_t* sp_index, int32_t M, int32_t k,
+                                   float* grad_sp, hipStream_t stream) {
+  return run_sspmm(row_ptr, col_idx, val, n_dst, n_src, nnz, dy, sp_index, M, k,
+                   grad_sp, true, stream);
 }
 
 rtopk_status_t rtopk_maxk_backward(const float* grad_sp,

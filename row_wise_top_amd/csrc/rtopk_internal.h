@@ -126,6 +126,12 @@ constexpr int64_t kEdgesPerWave = 256;
 // nnz > 0, 1 <= k <= m <= kMaxRowLength).
 hipError_t launch_spgemm(SpgemmArgs a, bool u8_index, hipStream_t stream);
 
+// Enqueue the backward of the aggregation to the compressed features
+// (rtopk_spgemm.hip), with the same SpgemmArgs read as: sp_data = dY
+// ([n_dst, m]), sp_index the survivors' columns ([n_src, k]), y = grad_sp
+// ([n_src, k], zeroed, then accumulated).
+hipError_t launch_sspmm(SpgemmArgs a, bool u8_index, hipStream_t stream);
+
 // Enqueue the selection kernel for `a` on `stream`. Arguments are already
 // validated (1 <= k <= m <= kMaxRowLength, n > 0, u8 only with m <= 256).
 // Returns the HIP error of the launch.

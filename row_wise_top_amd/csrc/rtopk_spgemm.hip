@@ -217,7 +217,131 @@ __global__ __launch_bounds__(kBlock) void spgemm_rows(SpgemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Backward to the compressed features (SSpMM): grad_sp[j, t] = sum over the
+// edges e = (i -> j) of val[e] * dY[i, sp_index[j, t]], i.e. A^T dY sampled
+// at the survivors (review page: the backward reuses the forward's pattern
+// with an outer-product dataflow and dense-row prefetching). The same CSR of
+// A as the forward: wave w takes edges [w*C, (w+1)*C); for each row i with
+// edges there it loads the dense row dY[i, :] into LDS once (coalesced),
+// then every edge (i -> j) adds val * dY[i, sp_index[j, :]] into the k
+// contiguous floats of grad_sp[j, :] with float atomics (grad_sp zeroed
+// first). Lanes map to (edge slot, survivor) as in the forward.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kBlock) void zero_floats(float* p, int64_t count) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; q < count;
+       q += stride)
+    p[q] = 0.0f;
+}
+
+template <typename IdxT>
+__global__ __launch_bounds__(kBlock) void sspmm_rows(SpgemmArgs a) {
+  extern __shared__ float lds[];
+  const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+  const int wave_in_block =
+      __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  // Per wave: the dense dY row (m_pad floats), then the staged edge range.
+  float* dyrow = lds + static_cast<int64_t>(wave_in_block) * (a.m_pad + 2 * kEdgesPerWave);
+  int* ecol = reinterpret_cast<int*>(dyrow + a.m_pad);
+  float* eval = dyrow + a.m_pad + kEdgesPerWave;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * a.waves_per_block + wave_in_block;
+  if (w >= a.waves || a.nnz == 0) return;
+  const int64_t nnz = a.nnz;
+  const int64_t e0 = w * a.chunk;
+  const int64_t e1 = e0 + a.chunk < nnz ? e0 + a.chunk : nnz;
+  for (int j = lane; j < kEdgesPerWave; j += kWave) {
+    const int64_t e = e0 + j < e1 ? e0 + j : e1 - 1;
+    ecol[j] = a.col[e];
+    eval[j] = a.val[e];
+  }
+  __builtin_amdgcn_wave_barrier();
+  const int k = a.k;
+  const int P = a.slots;
+  const int lane_edge = k <= kWave ? (lane < P * k ? lane / k : -1) : 0;
+  const int lane_t = k <= kWave ? lane % k : lane;
+  const int addr_edge = lane_edge < 0 ? 0 : lane_edge;
+  const IdxT* sidx = static_cast<const IdxT*>(a.sp_index);
+  const float* dy = a.sp_data;  // the backward's dense input, [n_dst, m]
+  // Rows with edges in [e0, e1): from the row holding edge e0 on.
+  for (int64_t i = last_row_at_or_before(a.row_ptr, a.n_dst, e0, lane); i < a.n_dst; ++i) {
+    const int64_t rs = clamp_edge(a.row_ptr[i], nnz);
+    if (rs >= e1) break;
+    const int64_t re = clamp_edge(a.row_ptr[i + 1], nnz);
+    const int64_t s0 = rs > e0 ? rs : e0;
+    const int64_t s1 = re < e1 ? re : e1;
+    if (s0 >= s1) continue;
+    // Dense-row prefetch: dY[i, :] into LDS.
+    for (int c = lane; c < a.m; c += kWave) dyrow[c] = dy[i * a.m + c];
+    __builtin_amdgcn_wave_barrier();
+    constexpr int U = 8;  // steps whose index loads are issued together
+    for (int64_t b0 = s0; b0 < s1; b0 += static_cast<int64_t>(U) * P) {
+      for (int t0 = lane_t; t0 < k; t0 += kWave) {
+        int c[U];
+        float wv[U];
+        int64_t dst[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t e = b0 + static_cast<int64_t>(u) * P + addr_edge;
+          const int64_t ec = e < s1 ? e : s1 - 1;
+          const int j = ecol[ec - e0];
+          wv[u] = eval[ec - e0];
+          const bool live = lane_edge >= 0 && e < s1 &&
+                            static_cast<uint64_t>(static_cast<int64_t>(j)) <
+                                static_cast<uint64_t>(a.n_src);
+          const int64_t jj = live ? j : 0;
+          c[u] = static_cast<int>(sidx[jj * k + t0]);
+          dst[u] = jj * k + t0;
+          ok[u] = live;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (ok[u] && static_cast<uint32_t>(c[u]) < static_cast<uint32_t>(a.m))
+            unsafeAtomicAdd(a.y + dst[u], wv[u] * dyrow[c[u]]);  // hardware float atomic
+        }
+        if (k <= kWave) break;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 }  // namespace spgemm_detail
+
+hipError_t launch_sspmm(SpgemmArgs a, bool u8_index, hipStream_t stream) {
+  using namespace spgemm_detail;
+  const int64_t count = a.n_src * a.k;
+  if (count > 0) {
+    int64_t zb = (count + kBlock - 1) / kBlock;
+    zb = zb < 65536 ? zb : 65536;
+    hipLaunchKernelGGL(zero_floats, dim3(static_cast<uint32_t>(zb)), dim3(kBlock), 0,
+                       stream, a.y, count);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (a.nnz == 0) return hipSuccess;
+  a.chunk = kEdgesPerWave;
+  a.waves = (a.nnz + a.chunk - 1) / a.chunk;
+  a.m_pad = (a.m + 3) & ~3;
+  a.slots = a.k <= kWave ? (kWave / a.k < 4 ? kWave / a.k : 4) : 1;
+  const int per_wave_bytes =
+      (a.m_pad + 2 * static_cast<int>(kEdgesPerWave)) * static_cast<int>(sizeof(float));
+  int wpb = 65536 / per_wave_bytes;
+  a.waves_per_block = wpb < 1 ? 1 : (wpb > kWavesPerBlock ? kWavesPerBlock : wpb);
+  const int64_t blocks = (a.waves + a.waves_per_block - 1) / a.waves_per_block;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const size_t lds = static_cast<size_t>(a.waves_per_block) * per_wave_bytes;
+  const dim3 block(kWave * a.waves_per_block);
+  if (u8_index)
+    hipLaunchKernelGGL(sspmm_rows<uint8_t>, dim3(static_cast<uint32_t>(blocks)), block, lds,
+                       stream, a);
+  else
+    hipLaunchKernelGGL(sspmm_rows<int32_t>, dim3(static_cast<uint32_t>(blocks)), block, lds,
+                       stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_spgemm(SpgemmArgs a, bool u8_index, hipStream_t stream) {
   using namespace spgemm_detail;

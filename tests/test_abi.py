@@ -26,7 +26,8 @@ def test_header_declares_expected_entry_points():
         "rtopk_select_exact_u8", "rtopk_select_bucketed", "rtopk_select_bucketed_u8",
         "rtopk_maxk_forward", "rtopk_maxk_forward_u8",
         "rtopk_maxk_backward", "rtopk_maxk_backward_u8", "rtopk_cbsr_spgemm",
-        "rtopk_cbsr_spgemm_u8", "rtopk_status_string"])
+        "rtopk_cbsr_spgemm_u8", "rtopk_cbsr_sspmm", "rtopk_cbsr_sspmm_u8",
+        "rtopk_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -226,6 +227,32 @@ def test_spgemm_u8_requires_short_rows():
 @pytest.mark.parametrize("fn", SPGEMM)
 @pytest.mark.parametrize("which", [0, 1, 2, 3, 4, 5])
 def test_spgemm_null_pointers(fn, which):
+    ptrs = [FAKE] * 6
+    ptrs[which] = None
+    assert call(fn, ptrs[0], ptrs[1], ptrs[2], 4, 4, 4, ptrs[3], ptrs[4], 16, 4,
+                ptrs[5], None) == 1
+
+
+SSPMM = ["rtopk_cbsr_sspmm", "rtopk_cbsr_sspmm_u8"]
+
+
+@pytest.mark.parametrize("fn", SSPMM)
+def test_sspmm_no_source_rows_is_a_noop(fn):
+    assert call(fn, None, None, None, 4, 0, 0, None, None, 16, 4, None, None) == 0
+
+
+@pytest.mark.parametrize("fn", SSPMM)
+@pytest.mark.parametrize("n_dst,n_src,nnz,m,k,code", [
+    (-1, 4, 4, 16, 4, 1), (4, -1, 4, 16, 4, 1), (4, 4, -1, 16, 4, 1),
+    (4, 0, 4, 16, 4, 1), (4, 4, 4, 16, 17, 1), (4, 4, 4, 8193, 4, 2),
+])
+def test_sspmm_argument_errors(fn, n_dst, n_src, nnz, m, k, code):
+    assert call(fn, FAKE, FAKE, FAKE, n_dst, n_src, nnz, FAKE, FAKE, m, k, FAKE, None) == code
+
+
+@pytest.mark.parametrize("fn", SSPMM)
+@pytest.mark.parametrize("which", [0, 1, 2, 3, 4, 5])
+def test_sspmm_null_pointers(fn, which):
     ptrs = [FAKE] * 6
     ptrs[which] = None
     assert call(fn, ptrs[0], ptrs[1], ptrs[2], 4, 4, 4, ptrs[3], ptrs[4], 16, 4,

@@ -1,9 +1,11 @@
 """GPU parity of the MaxK-GNN forward aggregation (rtopk_cbsr_spgemm[_u8])
-against oracle.spgemm.
+against oracle.spgemm, and of its backward to the compressed features
+(rtopk_cbsr_sspmm[_u8]) against oracle.sspmm.
 
-The kernel sums in single precision in an order of its own (LDS float atomics
-within a row, global float atomics for rows cut between two waves' edge
-ranges), so the bar is the error bound of floating-point summation: every
+The kernels sum in single precision in an order of their own (forward: LDS
+accumulator rows per edge slot, summed at the end, and global float atomics
+for rows cut between two waves' edge ranges; backward: global float atomics
+per edge), so the bar is the error bound of floating-point summation: every
 element must satisfy
 
     |y_gpu - y_exact| <= (d + 2) * 2^-24 * sum |val * x|  +  2^-126,
@@ -138,3 +140,78 @@ def test_full_size_graph():
     x = workloads.config_input(3, n, m)
     sd, si = oracle.exact(x, k)
     check(rp, ci, va, sd, si, m, "262144 nodes, mean degree 64, u8", u8=True)
+
+
+# --------------------------------------------------------------------------
+# Backward to the compressed features (rtopk_cbsr_sspmm[_u8]) against
+# oracle.sspmm. Bound: (d + 2) * 2^-24 * sum |terms| + 2^-126 per element,
+# d the number of edges into the source row.
+# --------------------------------------------------------------------------
+
+def run_gpu_sspmm(rp, ci, va, dy, si, u8=False):
+    import row_wise_top_amd as rt
+    d = torch.device("cuda:0")
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a).astype(dt)).to(d)
+    g = rt.rtopk_cbsr_sspmm(t(rp, np.int64), t(ci, np.int32), t(va, np.float32),
+                            t(dy, np.float32), t(si, np.uint8 if u8 else np.int32))
+    torch.cuda.synchronize()
+    return g.cpu().numpy()
+
+
+def check_sspmm(rp, ci, va, dy, si, label, u8=False):
+    want, absum = oracle.sspmm(rp, ci, va, dy, si, return_absum=True)
+    got = run_gpu_sspmm(rp, ci, va, dy, si, u8)
+    n_src = si.shape[0]
+    ok = (ci >= 0) & (ci < n_src)
+    indeg = np.bincount(ci[ok], minlength=n_src).astype(np.float64)
+    tol = (indeg[:, None] + 2.0) * 2.0 ** -24 * absum.astype(np.float64) + 2.0 ** -126
+    err = np.abs(got.astype(np.float64) - want.astype(np.float64))
+    bad = np.argwhere(err > tol)
+    assert bad.size == 0, (f"{label}: {len(bad)} elements outside the bound, first {bad[0]}: "
+                           f"got {got[tuple(bad[0])]} want {want[tuple(bad[0])]}")
+    assert np.all(got[absum == 0] == 0), f"{label}: nonzero where no term lands"
+
+
+@pytest.mark.parametrize("n_dst,n_src,mean,cap,m,k", [
+    (3000, 2000, 20.0, 500, 256, 32),
+    (5000, 5000, 64.0, 4096, 256, 32),
+    (2000, 800, 8.0, 100, 128, 16),
+    (1000, 700, 12.0, 300, 1024, 100),
+    (300, 400, 5.0, 50, 100, 7),
+])
+def test_sspmm_power_law_graphs(n_dst, n_src, mean, cap, m, k):
+    rp, ci, va = workloads.power_law_graph(n_dst, n_src, mean, cap, seed=2 * n_dst + m)
+    _, si = features(n_src, m, k, seed=9 + k, kind="maxk" if k <= 64 else "perm")
+    dy = workloads.normal(n_dst, m, 70 + m)
+    check_sspmm(rp, ci, va, dy, si, f"int32 {n_dst}x{m} k={k}")
+    if m <= 256:
+        check_sspmm(rp, ci, va, dy, si, f"u8 {n_dst}x{m} k={k}", u8=True)
+
+
+def test_sspmm_huge_row_and_edge_cases():
+    rng = np.random.default_rng(61)
+    deg = np.array([3, 0, 5, 20000, 0, 0, 7, 1, 0, 300])
+    rp = np.concatenate([[0], np.cumsum(deg)]).astype(np.int64)
+    n_src, m, k = 1000, 256, 32
+    ci = rng.integers(0, n_src, size=rp[-1]).astype(np.int32)
+    va = rng.standard_normal(rp[-1]).astype(np.float32)
+    _, si = features(n_src, m, k, seed=62)
+    dy = workloads.normal(len(deg), m, 63)
+    check_sspmm(rp, ci, va, dy, si, "huge row", u8=True)
+    # No edges: every gradient entry is zero.
+    rp0 = np.zeros(11, dtype=np.int64)
+    check_sspmm(rp0, np.zeros(0, np.int32), np.zeros(0, np.float32), dy, si, "no edges")
+    # Out-of-range edges and survivors.
+    ci2 = ci.copy()
+    ci2[::9] = n_src + 1
+    si2 = si.copy()
+    si2[::5, 2] = m + 7
+    check_sspmm(rp, ci2, va, dy, si2, "out of range")
+
+
+def test_sspmm_full_size_graph():
+    n, m, k = 262144, 256, 32
+    rp, ci, va = workloads.power_law_graph(n, n, 64.0, 4096, seed=48)
+    _, si = oracle.exact(workloads.config_input(3, n, m), k)
+    dy = workloads.normal(n, m, 64)
+    check_sspmm(rp, ci, va, dy, si, "262144 nodes, mean degree 64, u8", u8=True)
