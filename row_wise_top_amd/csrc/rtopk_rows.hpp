@@ -656,7 +656,7 @@ __device__ __forceinline__ void exact_row(const float (&vin)[Q],
 }
 
 // ---------------------------------------------------------------------------
-// The kernel: persistent waves, one row at a time, next rows prefetched.
+// The kernel: each wave takes groups of rows, one row at a time.
 // ---------------------------------------------------------------------------
 template <int Q, bool FULL, Mode MODE, int QC, typename Out>
 __device__ __forceinline__ void process_row(const float (&v)[Q],
@@ -669,23 +669,27 @@ __device__ __forceinline__ void process_row(const float (&v)[Q],
     capped_row<Q, FULL>(v, a, lane, out);
 }
 
-// Rows each wave keeps in flight (rows_in_flight in rtopk_internal.h): the
-// row being worked on plus D - 1 prefetched ones. The prefetch loads are
-// unconditional (past the last row they re-read it) so that the compiler's
-// wait counts stay exact and a wave only ever waits for the row it is about
-// to use. Four rows in flight for rows of at most 256 (measured faster than
-// two or three; 39 VGPRs keep 8 waves per SIMD).
+// Rows each wave keeps in flight (rows_in_flight in rtopk_internal.h): a
+// group of D consecutive rows whose loads are all issued before the first
+// of them is worked on. Four rows for rows of at most 256 (measured faster
+// than two or three; 39 VGPRs keep 8 waves per SIMD).
 template <int Q>
 constexpr int prefetch_depth() {
   return rows_in_flight(Q);
 }
 
 // Row order. Wave w of S works through groups of D consecutive rows:
-// group g is rows (g*S + w)*D ... (g*S + w)*D + D - 1. The rows a wave has in
-// flight are neighbours, and at any moment all waves together read one
-// contiguous stretch of the matrix (HBM streams fastest that way). For short
-// rows the host launches enough waves for one group each; the loop below
-// then runs once.
+// group g is rows (g*S + w)*D ... (g*S + w)*D + D - 1, so at any moment all
+// waves together read one contiguous stretch of the matrix (HBM streams
+// fastest that way). For short rows the host launches enough waves for one
+// group each and the group loop runs once; long rows (D = 1) get a
+// persistent grid.
+//
+// A group's loads are issued together, before any of its stores: loads and
+// stores of a wave complete in issue order on one counter, so waiting for a
+// row never waits for the stores of the rows before it. Rows past the end
+// of the matrix re-read the last row (the loads stay unconditional and the
+// compiler's wait counts exact) and are not processed.
 template <int Q, bool FULL, Mode MODE, int QC, typename IdxT>
 __global__ __launch_bounds__(kBlock) void rows_in_registers(SelectArgs a) {
   // Per wave: the LDS staging area of the exact search, (value, column)
@@ -696,6 +700,7 @@ __global__ __launch_bounds__(kBlock) void rows_in_registers(SelectArgs a) {
   // spare word per lane.
   constexpr bool kDense = MODE == Mode::kMaxk;
   constexpr int kDenseWords = kDense ? kWave * (Q + 1) : 1;
+  constexpr bool kBuckets = MODE == Mode::kBucket;
   __shared__ uint32_t scratch_all[kWavesPerBlock][kScratch];
   __shared__ uint32_t dense_all[kWavesPerBlock][kDenseWords];
   const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
@@ -706,47 +711,30 @@ __global__ __launch_bounds__(kBlock) void rows_in_registers(SelectArgs a) {
   const uint32_t spare = static_cast<uint32_t>(kWave * Q + lane);
   const int64_t waves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
   const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_in_block;
-  int64_t r = w * D;  // first row of the current group
-  if (r >= a.n) return;
-  // Rows this wave will process: D per full group of D*waves rows, plus the
-  // part of its last group before the end (at least one row: r < n).
-  const int64_t group_rows = waves * D;
-  int rows_left;
-  {
-    const int64_t rem = a.n - r;
-    const int64_t g = rem / group_rows;
-    const int64_t tail = rem - g * group_rows;
-    const int64_t total = g * D + (tail < D ? tail : D);
-    rows_left = total < 0x7fffffff ? static_cast<int>(total) : 0x7fffffff;
-  }
-  // Pointers advance by constant steps (no per-row 64-bit multiply).
-  const int64_t m = a.m, k = a.k;
-  const float* xg = a.x + r * m;  // current group
-  float* og = a.out_val + r * k;
-  IdxT* ig = static_cast<IdxT*>(a.out_idx) + r * k;
-  float* yg = kDense ? a.dense + r * m : nullptr;
-  // kBucket: bucket index of row r within its input row, and the group's
-  // first row (rows within a group are consecutive, so the index advances
-  // with a wrap; one 64-bit remainder per group).
-  constexpr bool kBuckets = MODE == Mode::kBucket;
-  int64_t rg = r;
-  int bucket = kBuckets ? static_cast<int>(r % a.buckets) : 0;
-  float buf[D][Q];
-  // Unconditional loads (rows past this wave's last one re-read its last
-  // row) so that the compiler's wait counts need no worst-case assumption.
+  const int64_t stride = waves * D;
+#pragma unroll 1
+  for (int64_t r = w * D; r < a.n; r += stride) {
+    const int rows = a.n - r < D ? static_cast<int>(a.n - r) : D;
+    const float* xg = a.x + r * a.m;
+    float buf[D][Q];
 #pragma unroll
-  for (int d = 0; d + 1 < D; ++d)
-    load_row<Q, FULL>(xg + min(d, rows_left - 1) * m, a.m, lane, buf[d]);
-  for (;;) {
+    for (int d = 0; d < D; ++d)
+      load_row<Q, FULL>(xg + min(d, rows - 1) * a.m, a.m, lane, buf[d]);
+    float* og = a.out_val + r * a.k;
+    IdxT* ig = static_cast<IdxT*>(a.out_idx) + r * a.k;
+    float* yg = kDense ? a.dense + r * a.m : nullptr;
+    // kBucket: bucket index of row r within its input row; rows of a group
+    // are consecutive, so it then advances with a wrap.
+    int bucket = 0;
+    if constexpr (kBuckets) {
+      bucket = r < 0x100000000LL
+                   ? static_cast<int>(static_cast<uint32_t>(r) %
+                                      static_cast<uint32_t>(a.buckets))
+                   : static_cast<int>(r % a.buckets);
+    }
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      // buf[d] holds row r + d. Refill the buffer freed by the previous row
-      // with the row D - 1 places further on in this wave's order (or, past
-      // its last row, re-read the current group's first row: a valid row).
-      const float* p = d == 0 ? xg + (D - 1) * m : xg + (group_rows + d - 1) * m;
-      load_row<Q, FULL>(d + D - 1 < rows_left ? p : xg, a.m, lane,
-                        buf[(d + D - 1) % D]);
-      if (d >= rows_left) return;
+      if (d >= rows) break;
       if constexpr (kDense) {
 #pragma unroll
         for (int s = 0; s < Q; ++s) dense[s * kWave + lane] = 0u;
@@ -756,30 +744,20 @@ __global__ __launch_bounds__(kBlock) void rows_in_registers(SelectArgs a) {
       }
       process_row<Q, FULL, MODE, QC>(
           buf[d], a, lane, scratch,
-          OutRow<IdxT, MODE>(og + d * k, ig + d * k, a.k, dense, spare,
+          OutRow<IdxT, MODE>(og + d * a.k, ig + d * a.k, a.k, dense, spare,
                              bucket * a.m));
       if constexpr (kBuckets) bucket = bucket + 1 == a.buckets ? 0 : bucket + 1;
       if constexpr (kDense) {
         __builtin_amdgcn_wave_barrier();
         // The dense row, stores past its end dropped.
         const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
-            yg + d * m, 0, a.m * 4, kRsrcWord3);
+            yg + d * a.m, 0, a.m * 4, kRsrcWord3);
 #pragma unroll
         for (int s = 0; s < Q; ++s)
           __builtin_amdgcn_raw_buffer_store_b32(dense[s * kWave + lane], ry,
                                                 (s * kWave + lane) * 4, 0, 0);
         __builtin_amdgcn_wave_barrier();
       }
-    }
-    rows_left -= D;
-    if (rows_left <= 0) return;
-    xg += group_rows * m;
-    og += group_rows * k;
-    ig += group_rows * k;
-    if constexpr (kDense) yg += group_rows * m;
-    if constexpr (kBuckets) {
-      rg += group_rows;
-      bucket = static_cast<int>(rg % a.buckets);
     }
   }
 }
