@@ -76,10 +76,11 @@ rtopk_status_t run_maxk_forward(const float* x, int64_t n, int32_t m, int32_t k,
   return err == hipSuccess ? RTOPK_SUCCESS : RTOPK_ERROR_LAUNCH;
 }
 
-// Bucketed top-k: the exact kernel over the [n * buckets, m / buckets] view
-// of x (each bucket a row, k / buckets survivors), emitted columns offset by
-// the bucket's position; the [n, k] outputs are the [n * buckets,
-// k / buckets] outputs of that view.
+// Bucketed top-k over the [n * buckets, m / buckets] view of x (each bucket
+// a row, k / buckets survivors), emitted columns offset by the bucket's
+// position; the [n, k] outputs are the [n * buckets, k / buckets] outputs of
+// that view. Short buckets take one lane each (rtopk_bucket.hip), longer
+// ones the exact wave-per-row kernel.
 rtopk_status_t run_bucketed(const float* x, int64_t n, int32_t m, int32_t k,
                             int32_t buckets, float* out_val, void* out_idx,
                             bool u8_index, hipStream_t stream) {
@@ -94,7 +95,10 @@ rtopk_status_t run_bucketed(const float* x, int64_t n, int32_t m, int32_t k,
   if (n == 0) return RTOPK_SUCCESS;
   rtopk::SelectArgs a{x,       n * buckets, width, k / buckets, -1, 0.0f,
                       out_val, out_idx,     0.0f,  0.0f,        nullptr, buckets};
-  const hipError_t err = rtopk::launch_select(a, rtopk::Mode::kBucket, u8_index, stream);
+  const hipError_t err =
+      rtopk::bucket_lanes_supported(width, k / buckets)
+          ? rtopk::launch_bucket_lanes(a, u8_index, stream)
+          : rtopk::launch_select(a, rtopk::Mode::kBucket, u8_index, stream);
   return err == hipSuccess ? RTOPK_SUCCESS : RTOPK_ERROR_LAUNCH;
 }
 

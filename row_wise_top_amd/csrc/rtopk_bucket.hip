@@ -1,0 +1,295 @@
+// Bucketed top-k with short buckets on gfx950 ("Approximate Top-k for
+// Increased Parallelism", abstract: many small independent top-k selections
+// in place of one). Each input row is split into b contiguous buckets of
+// w = m / b columns and each bucket keeps its kb = k / b largest elements
+// (ties to the lowest column), listed in column order.
+//
+// When buckets are short (w <= 32) a wave-wide search per bucket would leave
+// most lanes idle and pay the search's fixed cost b times per row. Here one
+// lane owns one bucket instead: it loads the bucket's w elements and finds
+// its kb best in registers. Up to two survivors: sorted insertion of
+// (value, column) pairs, strictly greater values moving up so that among
+// equal values the earlier column stays ahead. More: the kb largest values
+// by median-of-three insertion, then one pass in column order that keeps
+// every element above the kb-th largest value and the first few equal to it. A wave takes 64 consecutive buckets, so its
+// loads and stores cover one contiguous stretch of the input and of the
+// outputs; a lane reads its bucket with 16-byte loads where the layout
+// allows, and the lines a wave's loads share arrive once.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rtopk_internal.h"
+
+namespace rtopk {
+namespace bucket_detail {
+
+// Word 3 of a gfx9 buffer resource for untyped access (data format 32).
+constexpr int kRsrcWord3 = 0x00020000;
+// Cache policy of the bucket loads: the default one. The input is read once,
+// but the lanes of a wave share lines between their loads, and the kernel
+// reads survivors back from the bucket; non-temporal loads (gfx950 policy
+// bit 1) measured 109 -> 190 us at 262,144 x 256 with 8 buckets.
+constexpr int kLoadPolicy = 0;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// acc = 2 * acc + (x >= t), and the same with x == t: the compare's lane
+// mask is the carry-in of one add (two instructions, no mask logic).
+__device__ __forceinline__ void shift_in_ge(uint32_t& acc, float x, float t) {
+  asm("v_cmp_le_f32 vcc, %2, %1\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc"
+      : "+v"(acc)
+      : "v"(x), "v"(t)
+      : "vcc");
+}
+__device__ __forceinline__ void shift_in_eq(uint32_t& acc, float x, float t) {
+  asm("v_cmp_eq_f32 vcc, %2, %1\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc"
+      : "+v"(acc)
+      : "v"(x), "v"(t)
+      : "vcc");
+}
+
+// One lane per bucket row g (a.n of them): w = a.m <= W columns, kb = a.k
+// <= KB survivors, a.buckets buckets per input row. The bucket's elements
+// are x[g*w, g*w + w) and its survivors go to entries [g*kb, g*kb + kb) of
+// the outputs, with columns relative to the input row ((g mod b) * w + j).
+// VEC: w is a multiple of 4 and x 16-byte aligned, so the bucket is read
+// with 16-byte loads.
+//
+// The buffer resources start at the wave's first bucket (they must be the
+// same for every lane) and end at the wave's last one or the end of the
+// arrays: lanes past the end read zeros and their stores are dropped.
+//
+// Buckets of more than 16 columns (W = 32) with 16-byte loads go through
+// LDS: a lane's 16-byte loads at a 128-byte stride would make every load
+// instruction touch 64 lines (measured: a load-only version of the kernel
+// ran at 95 us for 262,144 x 256 in 8 buckets, against 54 us with 16
+// columns). The wave instead reads its buckets as one contiguous stretch
+// and each lane takes its bucket from LDS.
+template <int W, int KB, bool VEC, typename IdxT>
+__global__ __launch_bounds__(kBlock) void bucket_lanes(SelectArgs a) {
+  constexpr bool kStage = VEC && W == 32;
+  // LDS row of a lane: 36 floats (16-byte aligned; the skew of 4 banks per
+  // row keeps 8 consecutive lanes on distinct banks for both the writes and
+  // the reads below).
+  constexpr int kStride = 36;
+  __shared__ u32x4 stage_all[kStage ? kWavesPerBlock : 1][kStage ? kWave * kStride / 4 : 1];
+  const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+  const int wave_in_block =
+      __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * kBlock + wave_in_block * kWave;
+  if (g0 >= a.n) return;
+  const int w = a.m, kb = a.k;
+  const int live = a.n - g0 < kWave ? static_cast<int>(a.n - g0) : kWave;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a.x + g0 * w), 0, live * w * 4, kRsrcWord3);
+  // Elements past the bucket (j >= w) belong to the next one and are never
+  // considered.
+  const int base = lane * w * 4;
+  float v[W];
+  u32x4* stage = stage_all[kStage ? wave_in_block : 0];
+  if constexpr (kStage) {
+    // Chunk c (16 bytes, c = 64 i + lane) of the wave's live * w floats
+    // belongs to bucket (4c) / w at place (4c) mod w (a multiple of 4: w is).
+    // The quotient through a float reciprocal is exact here: 4c < 2048 and
+    // (4c + 1/2) / w stays at least 1/(2w) away from an integer.
+    const float inv_w = 1.0f / static_cast<float>(w);
+    const int floats = live * w;
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) {
+      const int f = 4 * (i * kWave + lane);
+      const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(rx, f * 4, 0, kLoadPolicy);
+      const int bkt = static_cast<int>((static_cast<float>(f) + 0.5f) * inv_w);
+      if (f < floats) stage[(bkt * kStride + (f - bkt * w)) / 4] = q;
+    }
+    // LDS operations of one wave complete in issue order; the barrier keeps
+    // the compiler from moving the reads above the writes.
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < W; j += 4) {
+      const u32x4 q = stage[(lane * kStride + j) / 4];
+      v[j] = __uint_as_float(q.x);
+      v[j + 1] = __uint_as_float(q.y);
+      v[j + 2] = __uint_as_float(q.z);
+      v[j + 3] = __uint_as_float(q.w);
+    }
+  } else if constexpr (VEC) {
+#pragma unroll
+    for (int j = 0; j < W; j += 4) {
+      const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(rx, base + j * 4, 0, kLoadPolicy);
+      v[j] = __uint_as_float(q.x);
+      v[j + 1] = __uint_as_float(q.y);
+      v[j + 2] = __uint_as_float(q.z);
+      v[j + 3] = __uint_as_float(q.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < W; ++j)
+      v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, base + j * 4, 0, kLoadPolicy));
+  }
+  // Places past w hold the next bucket's elements: -inf takes them out of
+  // every comparison below (the inputs are finite).
+  if (w < W) {
+#pragma unroll
+    for (int j = 0; j < W; ++j) v[j] = j < w ? v[j] : -__builtin_inff();
+  }
+  // Column of the bucket's first element within the input row.
+  const uint32_t b = static_cast<uint32_t>(a.buckets);
+  const uint32_t r0 = g0 < 0x100000000LL ? static_cast<uint32_t>(g0) % b
+                                         : static_cast<uint32_t>(g0 % a.buckets);
+  const uint32_t first = ((r0 + static_cast<uint32_t>(lane)) % b) * static_cast<uint32_t>(w);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      a.out_val + g0 * kb, 0, live * kb * 4, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<IdxT*>(a.out_idx) + g0 * kb, 0,
+      live * kb * static_cast<int>(sizeof(IdxT)), kRsrcWord3);
+  // Entry i of the lane's output; places past kb store past the resources'
+  // end, where the hardware drops them.
+  auto put = [&](int i, float x, uint32_t col) {
+    const int e = i < kb ? lane * kb + i : (1 << 28);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rv, e * 4, 0, 0);
+    if constexpr (sizeof(IdxT) == 1)
+      __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(first + col), ri, e, 0, 0);
+    else
+      __builtin_amdgcn_raw_buffer_store_b32(first + col, ri, e * 4, 0, 0);
+  };
+  if constexpr (KB <= 2) {
+    // The KB best so far with their columns, largest first. Empty places
+    // hold -inf (inputs are finite, so the first KB elements always enter).
+    float tv[KB];
+    int tc[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      tv[i] = -__builtin_inff();
+      tc[i] = i;
+    }
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      // Straight-line code over all W places (no loop the compiler could
+      // roll up and index registers in).
+      const float x = v[j];
+      bool gt[KB];
+#pragma unroll
+      for (int i = 0; i < KB; ++i) gt[i] = x > tv[i];
+      // Insert x above every element it beats: place i takes the element of
+      // place i - 1 if x beats that one too, else x if x beats place i.
+#pragma unroll
+      for (int i = KB - 1; i > 0; --i) {
+        tv[i] = gt[i - 1] ? tv[i - 1] : (gt[i] ? x : tv[i]);
+        tc[i] = gt[i - 1] ? tc[i - 1] : (gt[i] ? j : tc[i]);
+      }
+      tv[0] = gt[0] ? x : tv[0];
+      tc[0] = gt[0] ? j : tc[0];
+    }
+    if constexpr (KB == 2) {
+      // Column order (with kb == 1 the second place is dropped anyway).
+      const bool sw = kb == 2 && tc[0] > tc[1];
+      const float v0 = tv[0];
+      const int c0 = tc[0];
+      tv[0] = sw ? tv[1] : tv[0];
+      tc[0] = sw ? tc[1] : tc[0];
+      tv[1] = sw ? v0 : tv[1];
+      tc[1] = sw ? c0 : tc[1];
+    }
+#pragma unroll
+    for (int i = 0; i < KB; ++i) put(i, tv[i], static_cast<uint32_t>(tc[i]));
+  } else {
+    // The KB largest values (a multiset, largest first) by median-of-three
+    // insertion: with tv sorted, place i becomes med3(tv[i-1], x, tv[i]).
+    float tv[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) tv[i] = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      const float x = v[j];
+#pragma unroll
+      for (int i = KB - 1; i > 0; --i) tv[i] = __builtin_amdgcn_fmed3f(tv[i - 1], x, tv[i]);
+      tv[0] = fmaxf(tv[0], x);
+    }
+    // The kb-th largest value and how many of the kb largest equal it.
+    float thr = tv[0];
+#pragma unroll
+    for (int i = 1; i < KB; ++i) thr = i < kb ? tv[i] : thr;
+    int need_eq = 0;
+#pragma unroll
+    for (int i = 0; i < KB; ++i) need_eq += (i < kb && tv[i] == thr) ? 1 : 0;
+    // Bit mask of the places at or above thr, place j at bit 31 - j (the
+    // mask doubles and takes the new bit: one shift-add per place, no
+    // lane-mask logic). Without surplus ties these are the survivors.
+    uint32_t keep = 0;
+#pragma unroll
+    for (int j = 0; j < W; ++j) shift_in_ge(keep, v[j], thr);
+    keep <<= 32 - W;
+    if (__builtin_amdgcn_ballot_w64(__builtin_popcount(keep) > kb) != 0) {
+      // Some lane has more elements equal to thr than the need_eq the kb
+      // largest hold: keep every place above thr and the need_eq lowest
+      // places (the highest bits) equal to it.
+      uint32_t equal = 0;
+#pragma unroll
+      for (int j = 0; j < W; ++j) shift_in_eq(equal, v[j], thr);
+      equal <<= 32 - W;
+      keep &= ~equal;
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        const uint32_t top = equal != 0u ? 0x80000000u >> __builtin_clz(equal) : 0u;
+        keep |= i < need_eq ? top : 0u;
+        equal ^= top;
+      }
+    }
+    // Emit them lowest column first. The value is read again from the
+    // bucket (from LDS, or from its line in the cache), which keeps the
+    // original bits.
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const int col = keep != 0u ? __builtin_clz(keep) : 0;
+      keep &= ~(0x80000000u >> col);
+      float x;
+      if constexpr (kStage)
+        x = reinterpret_cast<const float*>(stage)[lane * kStride + col];
+      else
+        x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, base + col * 4, 0, 0));
+      put(i, x, static_cast<uint32_t>(col));
+    }
+  }
+}
+
+template <int W, bool VEC, typename IdxT>
+RowsKernel pick_kb(int kb) {
+  if (kb <= 1) return bucket_lanes<W, 1, VEC, IdxT>;
+  if (kb <= 2) return bucket_lanes<W, 2, VEC, IdxT>;
+  if (kb <= 4) return bucket_lanes<W, 4, VEC, IdxT>;
+  return bucket_lanes<W, 8, VEC, IdxT>;
+}
+
+template <bool VEC, typename IdxT>
+RowsKernel pick_w(int w, int kb) {
+  if (w <= 8) return pick_kb<8, VEC, IdxT>(kb);
+  if (w <= 16) return pick_kb<16, VEC, IdxT>(kb);
+  return pick_kb<32, VEC, IdxT>(kb);
+}
+
+template <typename IdxT>
+RowsKernel pick(int w, int kb, bool vec) {
+  return vec ? pick_w<true, IdxT>(w, kb) : pick_w<false, IdxT>(w, kb);
+}
+
+}  // namespace bucket_detail
+
+bool bucket_lanes_supported(int width, int kb) {
+  return width <= kLaneBucketWidth && kb <= kLaneBucketSurvivors;
+}
+
+hipError_t launch_bucket_lanes(const SelectArgs& a, bool u8_index,
+                               hipStream_t stream) {
+  using namespace bucket_detail;
+  const bool vec = a.m % 4 == 0 && (reinterpret_cast<uintptr_t>(a.x) & 15u) == 0;
+  const RowsKernel fn =
+      u8_index ? pick<uint8_t>(a.m, a.k, vec) : pick<int32_t>(a.m, a.k, vec);
+  const int64_t blocks = (a.n + kBlock - 1) / kBlock;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(fn, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace rtopk

@@ -1,5 +1,6 @@
 // Internal interface between the C ABI (rtopk_api.hip) and the kernels
-// (rtopk_kernels.hip). Not installed; not part of the public ABI.
+// (rtopk_dispatch.hip and the rtopk_*.hip units it names). Not installed; not
+// part of the public ABI.
 #pragma once
 
 #include <stdint.h>
@@ -131,6 +132,16 @@ hipError_t launch_spgemm(SpgemmArgs a, bool u8_index, hipStream_t stream);
 // ([n_dst, m]), sp_index the survivors' columns ([n_src, k]), y = grad_sp
 // ([n_src, k], zeroed, then accumulated).
 hipError_t launch_sspmm(SpgemmArgs a, bool u8_index, hipStream_t stream);
+
+// Bucketed top-k with short buckets (rtopk_bucket.hip): one lane per bucket,
+// for buckets of at most kLaneBucketWidth columns keeping at most
+// kLaneBucketSurvivors each. `a` is the bucket view (n = rows * buckets,
+// m = bucket width, k = survivors per bucket, buckets = buckets per row).
+constexpr int kLaneBucketWidth = 32;
+constexpr int kLaneBucketSurvivors = 8;
+bool bucket_lanes_supported(int width, int kb);
+hipError_t launch_bucket_lanes(const SelectArgs& a, bool u8_index,
+                               hipStream_t stream);
 
 // Enqueue the selection kernel for `a` on `stream`. Arguments are already
 // validated (1 <= k <= m <= kMaxRowLength, n > 0, u8 only with m <= 256).

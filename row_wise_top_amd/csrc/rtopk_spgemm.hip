@@ -147,7 +147,8 @@ __device__ __forceinline__ void flush(const SpgemmArgs& a, int64_t i, float* acc
     if (cut)
       unsafeAtomicAdd(a.y + i * a.m + c, v);  // hardware float atomic
     else
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ry, c * 4, 0, 0);
+      // Non-temporal (gfx950 cache policy bit 1): y is written once.
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ry, c * 4, 0, 2);
   }
   __builtin_amdgcn_wave_barrier();
 }
@@ -175,8 +176,9 @@ __global__ __launch_bounds__(kBlock) void spgemm_rows(SpgemmArgs a) {
   // Stage the range's edges (coalesced; positions past e1 re-read e1 - 1).
   for (int j = lane; j < kEdgesPerWave; j += kWave) {
     const int64_t e = e0 + j < e1 ? e0 + j : e1 - 1;
-    ecol[j] = e >= 0 ? a.col[e] : 0;
-    eval[j] = e >= 0 ? a.val[e] : 0.0f;
+    // The CSR arrays are read once: non-temporal loads.
+    ecol[j] = e >= 0 ? __builtin_nontemporal_load(a.col + e) : 0;
+    eval[j] = e >= 0 ? __builtin_nontemporal_load(a.val + e) : 0.0f;
   }
   // LDS operations of one wave complete in issue order; the barrier keeps
   // the compiler from moving the reads below above these writes.
@@ -253,8 +255,9 @@ __global__ __launch_bounds__(kBlock) void sspmm_rows(SpgemmArgs a) {
   const int64_t e1 = e0 + a.chunk < nnz ? e0 + a.chunk : nnz;
   for (int j = lane; j < kEdgesPerWave; j += kWave) {
     const int64_t e = e0 + j < e1 ? e0 + j : e1 - 1;
-    ecol[j] = a.col[e];
-    eval[j] = a.val[e];
+    // The CSR arrays are read once: non-temporal loads.
+    ecol[j] = __builtin_nontemporal_load(a.col + e);
+    eval[j] = __builtin_nontemporal_load(a.val + e);
   }
   __builtin_amdgcn_wave_barrier();
   const int k = a.k;
@@ -273,7 +276,8 @@ __global__ __launch_bounds__(kBlock) void sspmm_rows(SpgemmArgs a) {
     const int64_t s1 = re < e1 ? re : e1;
     if (s0 >= s1) continue;
     // Dense-row prefetch: dY[i, :] into LDS.
-    for (int c = lane; c < a.m; c += kWave) dyrow[c] = dy[i * a.m + c];
+    for (int c = lane; c < a.m; c += kWave)
+      dyrow[c] = __builtin_nontemporal_load(dy + i * a.m + c);  // read once
     __builtin_amdgcn_wave_barrier();
     constexpr int U = 8;  // steps whose index loads are issued together
     for (int64_t b0 = s0; b0 < s1; b0 += static_cast<int64_t>(U) * P) {

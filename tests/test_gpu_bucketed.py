@@ -36,6 +36,12 @@ CASES = [  # (n, m, k, buckets)
     (500, 256, 32, 4), (77, 256, 64, 2), (64, 256, 256, 256), (99, 256, 16, 16),
     (60, 384, 24, 3), (50, 1000, 40, 4), (40, 1024, 64, 1), (33, 2048, 64, 2),
     (20, 3072, 48, 3), (17, 8192, 64, 8), (9, 8192, 512, 8),
+    # Buckets of at most 32 columns keeping at most 8 (one lane per bucket):
+    # every width class (8, 16, 32) and survivor class (1, 2, 4, 8), widths
+    # that are not multiples of 4, and survivors short of the class size.
+    (203, 12, 4, 4), (203, 12, 8, 4), (203, 12, 12, 4), (150, 40, 40, 8),
+    (150, 56, 56, 8), (97, 52, 24, 4), (97, 62, 16, 2), (300, 256, 64, 8),
+    (81, 96, 12, 4), (70, 2048, 512, 64), (66, 8192, 256, 256),
 ]
 
 
@@ -74,3 +80,20 @@ def test_bucketed_full_shape():
     x = workloads.config_input(3, 262144, 256)
     assert_identical(gpu_bucketed(x, 32, 8, u8=True), oracle.bucketed(x, 32, 8),
                      "262144 x 256 k=32 b=8")
+
+
+@pytest.mark.parametrize("m,k,b", [(256, 32, 8), (96, 12, 4), (64, 16, 16)])
+def test_bucketed_unaligned_input(m, k, b):
+    # A matrix starting one float past a 16-byte boundary: the short-bucket
+    # kernel then reads with 4-byte loads.
+    import row_wise_top_amd as rt
+    n = 211
+    x_np = workloads.normal(n, m, 700 + m)
+    flat = torch.zeros(n * m + 1, dtype=torch.float32, device="cuda:0")
+    x = flat[1:].view(n, m)
+    x.copy_(torch.from_numpy(x_np).to("cuda:0"))
+    assert x.data_ptr() % 16 != 0
+    v, i = rt.rtopk_select_bucketed(x, k, b)
+    torch.cuda.synchronize()
+    assert_identical((v.cpu().numpy(), i.cpu().numpy().astype(np.int32)),
+                     oracle.bucketed(x_np, k, b), f"unaligned m={m} k={k} b={b}")
