@@ -4,7 +4,7 @@
 // w = m / b columns and each bucket keeps its kb = k / b largest elements
 // (ties to the lowest column), listed in column order.
 //
-// When buckets are short (w <= 32) a wave-wide search per bucket would leave
+// When buckets are short (w <= 64) a wave-wide search per bucket would leave
 // most lanes idle and pay the search's fixed cost b times per row. Here one
 // lane owns one bucket instead: it loads the bucket's w elements and finds
 // its kb best in registers. Up to two survivors: sorted insertion of
@@ -60,24 +60,36 @@ __device__ __forceinline__ void shift_in_eq(uint32_t& acc, float x, float t) {
 // same for every lane) and end at the wave's last one or the end of the
 // arrays: lanes past the end read zeros and their stores are dropped.
 //
-// Buckets of more than 16 columns (W = 32) with 16-byte loads go through
+// Buckets of more than 16 columns (W >= 32) with 16-byte loads go through
 // LDS: a lane's 16-byte loads at a 128-byte stride would make every load
 // instruction touch 64 lines (measured: a load-only version of the kernel
 // ran at 95 us for 262,144 x 256 in 8 buckets, against 54 us with 16
 // columns). The wave instead reads its buckets as one contiguous stretch
 // and each lane takes its bucket from LDS.
+template <int W, bool VEC>
+constexpr bool lane_stage() {
+  return VEC && W >= 32;
+}
+// Waves per block: two for the 64-column stage (17 KB of LDS per wave).
+template <int W, bool VEC>
+constexpr int lane_waves() {
+  return lane_stage<W, VEC>() && W == 64 ? 2 : kWavesPerBlock;
+}
+
 template <int W, int KB, bool VEC, typename IdxT>
-__global__ __launch_bounds__(kBlock) void bucket_lanes(SelectArgs a) {
-  constexpr bool kStage = VEC && W == 32;
-  // LDS row of a lane: 36 floats (16-byte aligned; the skew of 4 banks per
-  // row keeps 8 consecutive lanes on distinct banks for both the writes and
-  // the reads below).
-  constexpr int kStride = 36;
-  __shared__ u32x4 stage_all[kStage ? kWavesPerBlock : 1][kStage ? kWave * kStride / 4 : 1];
+__global__ __launch_bounds__((lane_waves<W, VEC>() * kWave)) void bucket_lanes(SelectArgs a) {
+  constexpr bool kStage = lane_stage<W, VEC>();
+  constexpr int kWaves = lane_waves<W, VEC>();
+  // LDS row of a lane: W + 4 floats (16-byte aligned; the skew of 4 banks
+  // per row keeps 8 consecutive lanes on distinct banks for both the writes
+  // and the reads below).
+  constexpr int kStride = W + 4;
+  __shared__ u32x4 stage_all[kStage ? kWaves : 1][kStage ? kWave * kStride / 4 : 1];
   const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
   const int wave_in_block =
       __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * kBlock + wave_in_block * kWave;
+  const int64_t g0 =
+      static_cast<int64_t>(blockIdx.x) * (kWaves * kWave) + wave_in_block * kWave;
   if (g0 >= a.n) return;
   const int w = a.m, kb = a.k;
   const int live = a.n - g0 < kWave ? static_cast<int>(a.n - g0) : kWave;
@@ -91,7 +103,7 @@ __global__ __launch_bounds__(kBlock) void bucket_lanes(SelectArgs a) {
   if constexpr (kStage) {
     // Chunk c (16 bytes, c = 64 i + lane) of the wave's live * w floats
     // belongs to bucket (4c) / w at place (4c) mod w (a multiple of 4: w is).
-    // The quotient through a float reciprocal is exact here: 4c < 2048 and
+    // The quotient through a float reciprocal is exact here: 4c < 4096 and
     // (4c + 1/2) / w stays at least 1/(2w) away from an integer.
     const float inv_w = 1.0f / static_cast<float>(w);
     const int floats = live * w;
@@ -213,27 +225,47 @@ __global__ __launch_bounds__(kBlock) void bucket_lanes(SelectArgs a) {
     int need_eq = 0;
 #pragma unroll
     for (int i = 0; i < KB; ++i) need_eq += (i < kb && tv[i] == thr) ? 1 : 0;
-    // Bit mask of the places at or above thr, place j at bit 31 - j (the
-    // mask doubles and takes the new bit: one shift-add per place, no
-    // lane-mask logic). Without surplus ties these are the survivors.
-    uint32_t keep = 0;
+    // Bit masks of the places at or above thr: place j at bit 31 - (j mod
+    // 32) of word j / 32 (a mask doubles and takes the new bit: one
+    // shift-add per place, no lane-mask logic). Without surplus ties these
+    // are the survivors.
+    constexpr int NW = (W + 31) / 32;
+    uint32_t keep[NW];
+    int count = 0;
 #pragma unroll
-    for (int j = 0; j < W; ++j) shift_in_ge(keep, v[j], thr);
-    keep <<= 32 - W;
-    if (__builtin_amdgcn_ballot_w64(__builtin_popcount(keep) > kb) != 0) {
+    for (int q = 0; q < NW; ++q) {
+      constexpr int kLast = W < 32 ? W : 32;  // places per word
+      keep[q] = 0;
+#pragma unroll
+      for (int j = 0; j < kLast; ++j) shift_in_ge(keep[q], v[32 * q + j], thr);
+      keep[q] <<= 32 - kLast;
+      count += __builtin_popcount(keep[q]);
+    }
+    if (__builtin_amdgcn_ballot_w64(count > kb) != 0) {
       // Some lane has more elements equal to thr than the need_eq the kb
       // largest hold: keep every place above thr and the need_eq lowest
-      // places (the highest bits) equal to it.
-      uint32_t equal = 0;
+      // places (first words, highest bits) equal to it.
+      uint32_t equal[NW];
 #pragma unroll
-      for (int j = 0; j < W; ++j) shift_in_eq(equal, v[j], thr);
-      equal <<= 32 - W;
-      keep &= ~equal;
+      for (int q = 0; q < NW; ++q) {
+        constexpr int kLast = W < 32 ? W : 32;
+        equal[q] = 0;
+#pragma unroll
+        for (int j = 0; j < kLast; ++j) shift_in_eq(equal[q], v[32 * q + j], thr);
+        equal[q] <<= 32 - kLast;
+        keep[q] &= ~equal[q];
+      }
 #pragma unroll
       for (int i = 0; i < KB; ++i) {
-        const uint32_t top = equal != 0u ? 0x80000000u >> __builtin_clz(equal) : 0u;
-        keep |= i < need_eq ? top : 0u;
-        equal ^= top;
+        bool done = i >= need_eq;
+#pragma unroll
+        for (int q = 0; q < NW; ++q) {
+          const uint32_t top = equal[q] != 0u ? 0x80000000u >> __builtin_clz(equal[q]) : 0u;
+          const bool take = !done && top != 0u;
+          keep[q] |= take ? top : 0u;
+          equal[q] ^= take ? top : 0u;
+          done = done || take;
+        }
       }
     }
     // Emit them lowest column first. The value is read again from the
@@ -241,8 +273,16 @@ __global__ __launch_bounds__(kBlock) void bucket_lanes(SelectArgs a) {
     // original bits.
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
-      const int col = keep != 0u ? __builtin_clz(keep) : 0;
-      keep &= ~(0x80000000u >> col);
+      int col = 0;
+      bool found = false;
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        const bool here = !found && keep[q] != 0u;
+        const int c = keep[q] != 0u ? __builtin_clz(keep[q]) : 0;
+        col = here ? 32 * q + c : col;
+        keep[q] &= here ? ~(0x80000000u >> c) : ~0u;
+        found = found || here;
+      }
       float x;
       if constexpr (kStage)
         x = reinterpret_cast<const float*>(stage)[lane * kStride + col];
@@ -265,7 +305,8 @@ template <bool VEC, typename IdxT>
 RowsKernel pick_w(int w, int kb) {
   if (w <= 8) return pick_kb<8, VEC, IdxT>(kb);
   if (w <= 16) return pick_kb<16, VEC, IdxT>(kb);
-  return pick_kb<32, VEC, IdxT>(kb);
+  if (w <= 32) return pick_kb<32, VEC, IdxT>(kb);
+  return pick_kb<64, VEC, IdxT>(kb);
 }
 
 template <typename IdxT>
@@ -285,9 +326,11 @@ hipError_t launch_bucket_lanes(const SelectArgs& a, bool u8_index,
   const bool vec = a.m % 4 == 0 && (reinterpret_cast<uintptr_t>(a.x) & 15u) == 0;
   const RowsKernel fn =
       u8_index ? pick<uint8_t>(a.m, a.k, vec) : pick<int32_t>(a.m, a.k, vec);
-  const int64_t blocks = (a.n + kBlock - 1) / kBlock;
+  // Must match lane_waves() for the kernel picked.
+  const int threads = (vec && a.m > 32) ? 2 * kWave : kBlock;
+  const int64_t blocks = (a.n + threads - 1) / threads;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(fn, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0,
+  hipLaunchKernelGGL(fn, dim3(static_cast<uint32_t>(blocks)), dim3(threads), 0,
                      stream, a);
   return hipGetLastError();
 }

@@ -137,7 +137,7 @@ hipError_t launch_sspmm(SpgemmArgs a, bool u8_index, hipStream_t stream);
 // for buckets of at most kLaneBucketWidth columns keeping at most
 // kLaneBucketSurvivors each. `a` is the bucket view (n = rows * buckets,
 // m = bucket width, k = survivors per bucket, buckets = buckets per row).
-constexpr int kLaneBucketWidth = 32;
+constexpr int kLaneBucketWidth = 64;
 constexpr int kLaneBucketSurvivors = 8;
 bool bucket_lanes_supported(int width, int kb);
 hipError_t launch_bucket_lanes(const SelectArgs& a, bool u8_index,

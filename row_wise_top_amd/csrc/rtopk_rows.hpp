@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "rtopk_internal.h"
 
 namespace rtopk {
@@ -326,25 +328,28 @@ __device__ __forceinline__ void capped_row(const float (&vin)[Q],
   float lo = mn, hi = mx;
   const int k = a.k;
   int chi = -1;  // #{x >= hi} once a count has set hi
-  int steps = 0;
-  while (a.max_iter < 0 || steps < a.max_iter) {
-    if (hi - lo <= a.eps) break;
-    const float mid = 0.5f * lo + 0.5f * hi;
-    if (!(lo < mid && mid < hi)) break;
-    const int c = count_ge(v, mid);
-    ++steps;
-    if (c == k) {
-      lo = mid;
-      hi = mid;
-      chi = k;
-      break;
+  // Each step as specified, written so that the only branch is the exit
+  // test: a count of exactly k sets lo = hi = mid (and chi = k), after which
+  // the width test ends the search at the next step, exactly as the
+  // specified immediate stop would (nothing changes in between). With
+  // eps = 0 the width test is implied by lo < mid < hi and is left out.
+  auto search = [&](auto eps_zero) {
+#pragma unroll 1
+    for (int steps = 0; a.max_iter < 0 || steps < a.max_iter; ++steps) {
+      const float mid = 0.5f * lo + 0.5f * hi;
+      const bool wide = decltype(eps_zero)::value || hi - lo > a.eps;
+      if (!(wide && lo < mid && mid < hi)) break;
+      const int c = count_ge(v, mid);
+      // Value selects, not branches: lo, hi and chi stay uniform.
+      lo = c >= k ? mid : lo;
+      hi = c <= k ? mid : hi;
+      chi = c <= k ? c : chi;
     }
-    // Value selects, not a branch: keeps lo/hi in scalar registers.
-    const bool up = c > k;
-    lo = up ? mid : lo;
-    hi = up ? hi : mid;
-    chi = up ? chi : c;
-  }
+  };
+  if (a.eps == 0.0f)
+    search(std::true_type{});
+  else
+    search(std::false_type{});
   if (chi < 0) chi = count_ge(v, hi);
   emit_fill(v, [lane](int s) { return s * kWave + lane; }, lo, hi, k, chi, out);
 }

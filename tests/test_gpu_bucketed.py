@@ -36,12 +36,14 @@ CASES = [  # (n, m, k, buckets)
     (500, 256, 32, 4), (77, 256, 64, 2), (64, 256, 256, 256), (99, 256, 16, 16),
     (60, 384, 24, 3), (50, 1000, 40, 4), (40, 1024, 64, 1), (33, 2048, 64, 2),
     (20, 3072, 48, 3), (17, 8192, 64, 8), (9, 8192, 512, 8),
-    # Buckets of at most 32 columns keeping at most 8 (one lane per bucket):
-    # every width class (8, 16, 32) and survivor class (1, 2, 4, 8), widths
-    # that are not multiples of 4, and survivors short of the class size.
+    # Buckets of at most 64 columns keeping at most 8 (one lane per bucket):
+    # every width class (8, 16, 32, 64) and survivor class (1, 2, 4, 8),
+    # widths that are not multiples of 4, and survivors short of the class.
     (203, 12, 4, 4), (203, 12, 8, 4), (203, 12, 12, 4), (150, 40, 40, 8),
     (150, 56, 56, 8), (97, 52, 24, 4), (97, 62, 16, 2), (300, 256, 64, 8),
     (81, 96, 12, 4), (70, 2048, 512, 64), (66, 8192, 256, 256),
+    (120, 256, 32, 4), (90, 200, 20, 4), (77, 96, 8, 2), (60, 128, 2, 2),
+    (45, 132, 24, 3),
 ]
 
 
@@ -82,7 +84,7 @@ def test_bucketed_full_shape():
                      "262144 x 256 k=32 b=8")
 
 
-@pytest.mark.parametrize("m,k,b", [(256, 32, 8), (96, 12, 4), (64, 16, 16)])
+@pytest.mark.parametrize("m,k,b", [(256, 32, 8), (96, 12, 4), (64, 16, 16), (256, 32, 4)])
 def test_bucketed_unaligned_input(m, k, b):
     # A matrix starting one float past a 16-byte boundary: the short-bucket
     # kernel then reads with 4-byte loads.
