@@ -120,10 +120,20 @@ def workload_name(args) -> str:
             + f" idx={args.index}")
 
 
-# Name fragment of the kernel each op launches (for the counter records).
-OP_KERNEL = {"select": "rows_in_registers", "maxk_forward": "rows_in_registers",
-             "maxk_backward": "scatter_rows", "bucketed": "rows_in_registers",
-             "spgemm": "spgemm_rows", "sspmm": "sspmm_rows"}
+def op_kernel(args) -> str:
+    """Name fragment of the kernel the op launches, for the counter records
+    (specific enough to leave out the exact selection the approximate ops
+    run once for their quality figures)."""
+    if args.op == "maxk_backward":
+        return "scatter_rows"
+    if args.op in ("spgemm", "sspmm"):
+        return f"{args.op}_rows"
+    if args.op == "bucketed":
+        width, kb = args.m // args.buckets, args.k // args.buckets
+        return "bucket_lanes" if width <= 64 and kb <= 8 else "(rtopk::Mode)3"
+    if args.op == "maxk_forward":
+        return "(rtopk::Mode)2"
+    return "(rtopk::Mode)1" if args.mode == "exact" else "(rtopk::Mode)0"
 
 
 def parse():
@@ -173,7 +183,7 @@ def main():
               "GPU its own block of rows with no exchange).", file=sys.stderr)
         sys.exit(2)
     if args.record_traffic:
-        record_traffic(workload_name(args), OP_KERNEL[args.op], *args.record_traffic)
+        record_traffic(workload_name(args), op_kernel(args), *args.record_traffic)
         return
 
     import numpy as np

@@ -1,0 +1,105 @@
+"""Host logic of bench.py (no GPU): the counter calibration that turns two
+rocprofv3 --pmc runs into HBM bytes per launch, which kernel each op's
+counters are attributed to, the source-hash gate on stored traffic figures,
+and the refusal of multi-GPU runs."""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def write_counters(path, counter, rows):
+    """A counter_collection.csv with (kernel name, value in KiB) records."""
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, value in rows:
+            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+SEL = "void rtopk::rows_detail::rows_in_registers<4, true, (rtopk::Mode)1, 1, unsigned char>(rtopk::SelectArgs)"
+EXACT_REF = SEL
+CAPPED = "void rtopk::rows_detail::rows_in_registers<4, true, (rtopk::Mode)0, 0, unsigned char>(rtopk::SelectArgs)"
+NEG = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(...)>"
+
+
+def test_record_traffic_calibrates_both_counters(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    # The negation kernel moves 2^28 bytes each way; FETCH_SIZE reads half of
+    # that (as on gfx950), WRITE_SIZE all of it.
+    ref_kib = bench.COPY_REF_BYTES / 1024.0
+    write_counters(tmp_path / "f.csv", "FETCH_SIZE",
+                   [(SEL, 1000.0), (SEL, 1002.0), (NEG, ref_kib / 2)])
+    write_counters(tmp_path / "w.csv", "WRITE_SIZE", [(SEL, 160.0), (SEL, 160.0), (NEG, ref_kib)])
+    bench.record_traffic("wl", "(rtopk::Mode)1", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
+    rec = json.load(open(tmp_path / "traffic.json"))["wl"]
+    assert rec["fetch_scale"] == pytest.approx(2.0)
+    assert rec["write_scale"] == pytest.approx(1.0)
+    assert rec["fetch_bytes"] == pytest.approx(1001.0 * 1024 * 2)
+    assert rec["write_bytes"] == pytest.approx(160.0 * 1024)
+    assert rec["bytes_per_launch"] == pytest.approx(1001.0 * 2048 + 160.0 * 1024)
+    assert rec["kernel_hash"] == bench.kernel_source_hash()
+    # The stored figure is served back only while the sources are unchanged.
+    assert bench.measured_traffic("wl") == pytest.approx(rec["bytes_per_launch"])
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "changed")
+    assert bench.measured_traffic("wl") is None
+    assert bench.measured_traffic("other workload") is None
+
+
+def test_counters_of_other_kernels_are_left_out(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    ref_kib = bench.COPY_REF_BYTES / 1024.0
+    # A capped run also launches the exact selection once (quality figures):
+    # its record must not enter the capped kernel's mean.
+    write_counters(tmp_path / "f.csv", "FETCH_SIZE",
+                   [(CAPPED, 500.0), (CAPPED, 500.0), (EXACT_REF, 9999.0), (NEG, ref_kib / 2)])
+    write_counters(tmp_path / "w.csv", "WRITE_SIZE",
+                   [(CAPPED, 80.0), (EXACT_REF, 9999.0), (NEG, ref_kib)])
+    args = argparse.Namespace(op="select", mode="capped", m=256, k=32, buckets=1)
+    bench.record_traffic("capped", bench.op_kernel(args), str(tmp_path / "f.csv"),
+                         str(tmp_path / "w.csv"))
+    rec = json.load(open(tmp_path / "traffic.json"))["capped"]
+    assert rec["fetch_kib_raw"] == pytest.approx(500.0)
+    assert rec["write_kib_raw"] == pytest.approx(80.0)
+
+
+def test_missing_records_are_an_error(tmp_path):
+    write_counters(tmp_path / "f.csv", "FETCH_SIZE", [(SEL, 1.0)])
+    with pytest.raises(SystemExit):
+        bench._counter_means(str(tmp_path / "f.csv"), "FETCH_SIZE", "(rtopk::Mode)1")
+
+
+@pytest.mark.parametrize("op,mode,m,k,buckets,want", [
+    ("select", "exact", 256, 32, 1, "(rtopk::Mode)1"),
+    ("select", "capped", 256, 32, 1, "(rtopk::Mode)0"),
+    ("maxk_forward", "exact", 256, 32, 1, "(rtopk::Mode)2"),
+    ("maxk_backward", "exact", 256, 32, 1, "scatter_rows"),
+    ("bucketed", "exact", 256, 32, 8, "bucket_lanes"),
+    ("bucketed", "exact", 256, 32, 4, "bucket_lanes"),
+    ("bucketed", "exact", 256, 32, 2, "(rtopk::Mode)3"),
+    ("bucketed", "exact", 256, 64, 2, "(rtopk::Mode)3"),
+    ("spgemm", "exact", 256, 32, 1, "spgemm_rows"),
+    ("sspmm", "exact", 256, 32, 1, "sspmm_rows"),
+])
+def test_op_kernel(op, mode, m, k, buckets, want):
+    args = argparse.Namespace(op=op, mode=mode, m=m, k=k, buckets=buckets)
+    assert bench.op_kernel(args) == want
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
