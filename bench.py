@@ -364,6 +364,32 @@ def main():
         extra = {"edges": nnz, "edges_per_s": nnz / (avg_launch_ms * 1e-3),
                  "gather_bytes_per_launch": gather,
                  "gather_gbs": gather / (avg_launch_ms * 1e-3) / 1e9}
+        if args.op == "sspmm":
+            # Float-atomic reference: torch's index_add_ adding one k-float row
+            # per edge into a [n, k] array at the same destination rows (the
+            # edges' columns), from one cached source row, timed the same way:
+            # as many float atomics as the kernel issues (nnz * k), none of
+            # its gathers.
+            g_ref = torch.zeros(n, k, dtype=torch.float32, device=dev)
+            rows_ref = ci_t.long()
+            src_ref = torch.ones(1, k, dtype=torch.float32, device=dev).expand(nnz, k)
+            for _ in range(3):
+                g_ref.index_add_(0, rows_ref, src_ref)
+            a0 = torch.cuda.Event(enable_timing=True)
+            a1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a0.record(stream)
+            for _ in range(10):
+                g_ref.index_add_(0, rows_ref, src_ref)
+            a1.record(stream)
+            torch.cuda.synchronize()
+            ref_ms = a0.elapsed_time(a1) / 10
+            extra["atomic_reference"] = {
+                "what": "torch index_add_ of one k-float row per edge (nnz * k float atomics)",
+                "us": ref_ms * 1e3,
+                "float_atomics": nnz * k,
+                "kernel_over_reference": avg_launch_ms / ref_ms}
+            del g_ref, rows_ref, src_ref
     algo_bytes = int(n * per_row)
     achieved = algo_bytes / (avg_launch_ms * 1e-3) / 1e9
     workload = workload_name(args)
