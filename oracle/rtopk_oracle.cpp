@@ -111,20 +111,20 @@ void exact_row(const float* x, int M, int k, float* ov, int32_t* oi) {
 //
 // Reading of the "Approach" section used here (each choice is one the page
 // leaves open):
-//   * The search range starts as [min, max] of the row ("binary search over
-//     the value range").
+//   * The search range starts as [min, max] of the row (the page bisects
+//     over the row's value range).
 //   * One search step: stop if hi - lo <= eps (absolute width, single
 //     precision subtraction); mid = 0.5*lo + 0.5*hi (cannot overflow);
 //     stop if mid does not lie strictly inside (lo, hi); count the elements
 //     with x >= mid. A count equal to k ends the search with lo = hi = mid
-//     ("a threshold that selects k elements"); a larger count raises lo to
-//     mid, a smaller one lowers hi to mid.
+//     (the page looks for a threshold with exactly k elements at or above
+//     it); a larger count raises lo to mid, a smaller one lowers hi to mid.
 //   * max_iter caps the number of counts; max_iter < 0 means no cap.
 //   * Second pass: A = positions with x >= hi, B = positions with
 //     lo <= x < hi, both in ascending position. The survivors are the first k
-//     of A followed by B ("a second pass using the minimum to fill
-//     borderline ties", with "the minimum" read as the lower end of the
-//     search range, which starts at the row minimum and only rises).
+//     of A followed by B (the page fills borderline ties in a second pass
+//     from the minimum, read here as the lower end of the search range,
+//     which starts at the row minimum and only rises).
 //   * fill_from_row_min != 0 selects the literal alternative reading in which
 //     B = positions with row_min <= x < hi (the row minimum never moves). It
 //     exists only so that the two readings can be compared on data.
