@@ -580,7 +580,19 @@ __device__ __forceinline__ void read_candidates(const uint32_t* __restrict__ scr
 
 // Full-row search when the first count missed the candidate window: Newton
 // steps on the whole row (compacting as soon as a count lands in (k, W]),
-// then order-key bisection.
+// then order-key bisection on the whole row, preceded by snaps for some row
+// lengths. The snaps matter for rows with many equal values (each settles
+// one distinct value): on 16,384 rows of 512 with about 30 distinct values
+// and k = 256 (no candidate window fits) the search went from 50.1 to
+// 19.0 us, on rows of 4,096 with k = 64 from 182 to 107 us. For 16 and 32
+// slots they cost occupancy (VGPRs 147 -> 171 at 32 slots) and for 96 and
+// 128 slots register spills (up to 290 bytes), so those keep key bisection
+// alone.
+template <int Q>
+constexpr bool full_row_snaps() {
+  return Q <= 8 || Q == 64;
+}
+
 template <int Q, int QC, typename Out>
 __device__ __forceinline__ void exact_row_search(const float (&v)[Q], int k,
                                               int lane, float t, int c,
@@ -593,11 +605,12 @@ __device__ __forceinline__ void exact_row_search(const float (&v)[Q], int k,
   const float shift = -static_cast<float>(target2) * h;
   auto col = [lane](int s) { return s * kWave + lane; };
   float lo = -kInf, hi = kInf;
-  int chi = 0;
+  int clo = kWave * Q, chi = 0;  // #{x >= lo} (padding included), #{x >= hi}
 #pragma unroll 1
   for (int it = 1;; ++it) {
     const bool up = c > k;
     lo = up ? t : lo;
+    clo = up ? c : clo;
     hi = up ? hi : t;
     chi = up ? chi : c;
     if (it == kRowSteps) break;
@@ -618,7 +631,10 @@ __device__ __forceinline__ void exact_row_search(const float (&v)[Q], int k,
       }
     }
   }
-  finish_by_keys(v, col, k, lo, hi, chi, out);
+  if constexpr (full_row_snaps<Q>())
+    settle_candidates<Q>(v, col, k, lo, clo, hi, chi, out);
+  else
+    finish_by_keys(v, col, k, lo, hi, chi, out);
 }
 
 template <int Q, bool FULL, int QC, typename Out>
