@@ -50,6 +50,10 @@ namespace rtopk {
 namespace rows_detail {
 
 constexpr float kInf = __builtin_inff();
+// Word 3 of a gfx9 buffer resource for untyped 32-bit access (data format 32).
+constexpr int kRsrcWord3 = 0x00020000;
+// Cache policy of the row loads (gfx950 encoding, bit 1 = non-temporal).
+constexpr int kLoadNT = 2;
 
 // ---------------------------------------------------------------------------
 // Wave-level primitives
@@ -147,38 +151,44 @@ __device__ __forceinline__ float wave_max(float a) {
 // Row in registers
 // ---------------------------------------------------------------------------
 
-// Load a row into slots. FULL: the row length is exactly 64*Q. Otherwise
-// lanes past the end re-read the last element (always in bounds) so that the
-// loads stay unconditional; mask_tail() then replaces them. The input is
-// read once: non-temporal loads keep it from displacing other lines in the
-// caches (measured: the memory-only floor of the 262,144 x 256 selection
-// drops from 54 to 49.5 us).
+// Load a row into slots. FULL: the row length is exactly 64*Q. Otherwise the
+// row is read through a buffer resource of exactly m floats: positions past
+// the end read 0 (mask_tail() then makes them -inf), and every slot's load
+// is the lane's offset plus a constant, so no per-slot address stays live
+// (with clamped addresses the compiler kept one per slot across the row
+// loop: 256 VGPRs and thousands of spill instructions at 128 slots). The
+// input is read once: non-temporal loads keep it from displacing other
+// lines in the caches (measured: the memory-only floor of the 262,144 x 256
+// selection drops from 54 to 49.5 us).
 template <int Q, bool FULL>
 __device__ __forceinline__ void load_row(const float* __restrict__ row, int m,
                                          int lane, float (&v)[Q]) {
+  if constexpr (FULL) {
 #pragma unroll
-  for (int s = 0; s < Q; ++s) {
-    int j = s * kWave + lane;
-    if (!FULL) j = min(j, m - 1);
-    v[s] = __builtin_nontemporal_load(row + j);
+    for (int s = 0; s < Q; ++s) v[s] = __builtin_nontemporal_load(row + s * kWave + lane);
+  } else {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(row), 0, m * 4, kRsrcWord3);
+#pragma unroll
+    for (int s = 0; s < Q; ++s)
+      v[s] = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(r, lane * 4, s * kWave * 4, kLoadNT));
   }
-}
-
-// Whether slot s of this lane holds a column of the row.
-template <bool FULL>
-__device__ __forceinline__ bool in_row(int s, int m, int lane) {
-  return FULL || s * kWave + lane < m;
 }
 
 // Positions past the end become -inf: no count and no selection test picks
 // them (every threshold used is finite or the bracket end +-inf, and the
-// tests are x >= t with t > -inf).
+// tests are x >= t with t > -inf). The row length goes through an empty asm
+// so that the per-slot tests are made here, once per row, and not hoisted
+// out of the row loop as one live lane mask per slot.
 template <int Q, bool FULL>
 __device__ __forceinline__ void mask_tail(int m, int lane, float (&v)[Q]) {
   if (FULL) return;
+  int mo = m;
+  asm volatile("" : "+s"(mo));
 #pragma unroll
   for (int s = 0; s < Q; ++s) {
-    if (!in_row<FULL>(s, m, lane)) v[s] = -kInf;
+    if (!(s * kWave + lane < mo)) v[s] = -kInf;
   }
 }
 
@@ -215,8 +225,7 @@ __device__ __forceinline__ float key_value(int32_t key) {
 // compiler's wait counts stay exact.
 // ---------------------------------------------------------------------------
 
-// Word 3 of a gfx9 buffer resource for untyped 32-bit access (data format 32).
-constexpr int kRsrcWord3 = 0x00020000;
+
 // Output position of a lane that stores nothing: past any row end, and times
 // four still a valid 32-bit offset.
 constexpr uint32_t kDropPos = 1u << 28;
@@ -281,6 +290,11 @@ template <int S, typename Out, typename ColFn>
 __device__ __forceinline__ void emit_fill(const float (&v)[S], ColFn col,
                                           float lo, float hi, int k, int nA,
                                           const Out& out) {
+  if constexpr (S > 32) {
+    // As in emit_ge: no lane masks kept alive from earlier counts.
+    asm volatile("" : "+v"(lo));
+    asm volatile("" : "+v"(hi));
+  }
   if (nA >= k) {
     // The exact searches reach this only with nA == k (no rank is dropped,
     // so the MaxK dense row gets exactly the k survivors).
@@ -316,15 +330,17 @@ __device__ __forceinline__ void capped_row(const float (&vin)[Q],
                                            const SelectArgs& a, int lane,
                                            const Out& out) {
   float v[Q];
+#pragma unroll
+  for (int s = 0; s < Q; ++s) v[s] = vin[s];
+  mask_tail<Q, FULL>(a.m, lane, v);
   float mn = kInf, mx = -kInf;
 #pragma unroll
   for (int s = 0; s < Q; ++s) {
-    v[s] = vin[s];
-    mn = fminf(mn, v[s]);  // re-read tail lanes hold a real element
+    // Tail positions hold -inf (inputs are finite): out of the minimum.
+    mn = fminf(mn, FULL || v[s] > -kInf ? v[s] : kInf);
     mx = fmaxf(mx, v[s]);
   }
   wave_reduce2<OpMin, OpMax>(mn, mx);
-  mask_tail<Q, FULL>(a.m, lane, v);
   float lo = mn, hi = mx;
   const int k = a.k;
   int chi = -1;  // #{x >= hi} once a count has set hi
@@ -401,6 +417,10 @@ __device__ __forceinline__ float next_float(float f) {
 template <int S, typename Out, typename ColFn>
 __device__ __forceinline__ void emit_ge(const float (&v)[S], ColFn col,
                                         float t, const Out& out) {
+  // Long rows: recompute the compares rather than let the compiler keep the
+  // lane masks of the count that found t alive (one SGPR pair per slot,
+  // spilled at 128 slots).
+  if constexpr (S > 32) asm volatile("" : "+v"(t));
   uint32_t base = 0;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
@@ -647,12 +667,12 @@ __device__ __forceinline__ void exact_row(const float (&vin)[Q],
   // Scale of the row for the model behind the thresholds (the model assumes
   // rows centred near zero; the Newton steps correct the first threshold
   // when they are not).
+  // (Tail positions were read as 0.)
   float s2 = 0.0f;
 #pragma unroll
   for (int s = 0; s < Q; ++s) {
-    const float x = in_row<FULL>(s, a.m, lane) ? vin[s] : 0.0f;
     v[s] = vin[s];
-    s2 = fmaf(x, x, s2);
+    s2 = fmaf(vin[s], vin[s], s2);
   }
   s2 = wave_sum(s2);
   mask_tail<Q, FULL>(a.m, lane, v);
