@@ -602,15 +602,15 @@ __device__ __forceinline__ void read_candidates(const uint32_t* __restrict__ scr
 // steps on the whole row (compacting as soon as a count lands in (k, W]),
 // then order-key bisection on the whole row, preceded by snaps for some row
 // lengths. The snaps matter for rows with many equal values (each settles
-// one distinct value): on 16,384 rows of 512 with about 30 distinct values
-// and k = 256 (no candidate window fits) the search went from 50.1 to
-// 19.0 us, on rows of 4,096 with k = 64 from 182 to 107 us. For 16 and 32
-// slots they cost occupancy (VGPRs 147 -> 171 at 32 slots) and for 96 and
-// 128 slots register spills (up to 290 bytes), so those keep key bisection
-// alone.
+// one distinct value); on 16,384 rows with about 30 distinct values: 512
+// columns, k = 256 (no candidate window fits) 50.1 -> 18.4 us; 4,096
+// columns, k = 64, 182 -> 107 us; 8,192 columns, k = 64, 374 -> 196 us. At
+// 16 and 32 slots they cost occupancy (VGPRs 65 -> 79 and 86 -> 113) for
+// rows that almost always land in the candidate window, so those keep key
+// bisection alone.
 template <int Q>
 constexpr bool full_row_snaps() {
-  return Q <= 8 || Q == 64;
+  return Q <= 8 || Q >= 64;
 }
 
 template <int Q, int QC, typename Out>
