@@ -118,11 +118,10 @@ void exact_model(SelectArgs& a, int qc) {
 hipError_t launch_select(const SelectArgs& args, Mode mode, bool u8_index,
                          hipStream_t stream) {
   SelectArgs a = args;
-  int qc = 0;
-  if (mode != Mode::kCapped) {
-    qc = candidate_slots(slot_bucket(a.m), a.k);
-    exact_model(a, qc);
-  }
+  // Candidate slots: the exact search compacts after its first count, the
+  // capped one once the bracket's lower end leaves at most 64*qc elements.
+  const int qc = candidate_slots(slot_bucket(a.m), a.k);
+  if (mode != Mode::kCapped) exact_model(a, qc);
   const RowsKernel fn = kernel_for(a.m, mode, u8_index, qc);
   if (fn == nullptr) return hipErrorInvalidValue;
   int device = 0;

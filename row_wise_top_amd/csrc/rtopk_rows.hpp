@@ -322,55 +322,6 @@ __device__ __forceinline__ void emit_fill(const float (&v)[S], ColFn col,
 }
 
 // ---------------------------------------------------------------------------
-// Capped search (rtopk_select): the specification in rtopk.h, step for step.
-// Invariant: #{x >= lo} >= k and (#{x >= hi} < k or hi == row max).
-// ---------------------------------------------------------------------------
-template <int Q, bool FULL, typename Out>
-__device__ __forceinline__ void capped_row(const float (&vin)[Q],
-                                           const SelectArgs& a, int lane,
-                                           const Out& out) {
-  float v[Q];
-#pragma unroll
-  for (int s = 0; s < Q; ++s) v[s] = vin[s];
-  mask_tail<Q, FULL>(a.m, lane, v);
-  float mn = kInf, mx = -kInf;
-#pragma unroll
-  for (int s = 0; s < Q; ++s) {
-    // Tail positions hold -inf (inputs are finite): out of the minimum.
-    mn = fminf(mn, FULL || v[s] > -kInf ? v[s] : kInf);
-    mx = fmaxf(mx, v[s]);
-  }
-  wave_reduce2<OpMin, OpMax>(mn, mx);
-  float lo = mn, hi = mx;
-  const int k = a.k;
-  int chi = -1;  // #{x >= hi} once a count has set hi
-  // Each step as specified, written so that the only branch is the exit
-  // test: a count of exactly k sets lo = hi = mid (and chi = k), after which
-  // the width test ends the search at the next step, exactly as the
-  // specified immediate stop would (nothing changes in between). With
-  // eps = 0 the width test is implied by lo < mid < hi and is left out.
-  auto search = [&](auto eps_zero) {
-#pragma unroll 1
-    for (int steps = 0; a.max_iter < 0 || steps < a.max_iter; ++steps) {
-      const float mid = 0.5f * lo + 0.5f * hi;
-      const bool wide = decltype(eps_zero)::value || hi - lo > a.eps;
-      if (!(wide && lo < mid && mid < hi)) break;
-      const int c = count_ge(v, mid);
-      // Value selects, not branches: lo, hi and chi stay uniform.
-      lo = c >= k ? mid : lo;
-      hi = c <= k ? mid : hi;
-      chi = c <= k ? c : chi;
-    }
-  };
-  if (a.eps == 0.0f)
-    search(std::true_type{});
-  else
-    search(std::false_type{});
-  if (chi < 0) chi = count_ge(v, hi);
-  emit_fill(v, [lane](int s) { return s * kWave + lane; }, lo, hi, k, chi, out);
-}
-
-// ---------------------------------------------------------------------------
 // Exact search (rtopk_select_exact).
 // Bracket invariant: #{x >= lo} = clo >= k > chi = #{x >= hi}, with
 // lo = -inf and hi = +inf allowed at the start. Every count at a threshold t
@@ -598,6 +549,93 @@ __device__ __forceinline__ void read_candidates(const uint32_t* __restrict__ scr
   __builtin_amdgcn_wave_barrier();
 }
 
+// ---------------------------------------------------------------------------
+// Capped search (rtopk_select): the specification in rtopk.h, step for step.
+// Invariant: #{x >= lo} >= k and (#{x >= hi} < k or hi == row max).
+//
+// Every threshold after a step that raised lo lies above lo, so once
+// #{x >= lo} fits the candidate window (64*QC), the remaining steps and the
+// tie fill only need the elements >= lo: they are compacted into QC slots
+// (as in the exact search) and the search carries on there, with QC
+// compares per count instead of Q and a fill over QC slots.
+// ---------------------------------------------------------------------------
+template <int Q, bool FULL, int QC, typename Out>
+__device__ __forceinline__ void capped_row(const float (&vin)[Q],
+                                           const SelectArgs& a, int lane,
+                                           uint32_t* __restrict__ scratch,
+                                           const Out& out) {
+  float v[Q];
+#pragma unroll
+  for (int s = 0; s < Q; ++s) v[s] = vin[s];
+  mask_tail<Q, FULL>(a.m, lane, v);
+  float mn = kInf, mx = -kInf;
+#pragma unroll
+  for (int s = 0; s < Q; ++s) {
+    // Tail positions hold -inf (inputs are finite): out of the minimum.
+    mn = fminf(mn, FULL || v[s] > -kInf ? v[s] : kInf);
+    mx = fmaxf(mx, v[s]);
+  }
+  wave_reduce2<OpMin, OpMax>(mn, mx);
+  float lo = mn, hi = mx;
+  const int k = a.k;
+  int clo = a.m;  // #{x >= lo}
+  int chi = -1;   // #{x >= hi} once a count has set hi
+  int steps = 0;
+  // One specified step on the elements in `w` (the row, or the candidates):
+  // false once the search has stopped. Only the exit is a branch: a count of
+  // exactly k sets lo = hi = mid (and chi = k), after which the width test
+  // ends the search at the next step, exactly as the specified immediate
+  // stop would (nothing changes in between). With eps = 0 the width test is
+  // implied by lo < mid < hi and is left out.
+  auto step = [&](const auto& w, auto eps_zero) {
+    if (!(a.max_iter < 0 || steps < a.max_iter)) return false;
+    const float mid = 0.5f * lo + 0.5f * hi;
+    const bool wide = decltype(eps_zero)::value || hi - lo > a.eps;
+    if (!(wide && lo < mid && mid < hi)) return false;
+    const int c = count_ge(w, mid);
+    ++steps;
+    // Value selects, not branches: lo, hi and the counts stay uniform.
+    lo = c >= k ? mid : lo;
+    clo = c >= k ? c : clo;
+    hi = c <= k ? mid : hi;
+    chi = c <= k ? c : chi;
+    return true;
+  };
+  auto search = [&](auto eps_zero) {
+#pragma unroll 1
+    for (;;) {
+      if constexpr (QC > 0) {
+        if (clo <= kWave * QC) break;
+      }
+      if (!step(v, eps_zero)) return false;
+    }
+    return true;  // stopped with the candidates fitting the window
+  };
+  const bool compact = a.eps == 0.0f ? search(std::true_type{}) : search(std::false_type{});
+  if constexpr (QC > 0) {
+    if (compact) {
+      count_and_stage<Q, QC>(v, lo, lane, scratch);
+      float cv[QC];
+      int ci[QC];
+      read_candidates<Q, QC>(scratch, clo, lane, cv, ci);
+      auto rest = [&](auto eps_zero) {
+#pragma unroll 1
+        while (step(cv, eps_zero)) {
+        }
+      };
+      if (a.eps == 0.0f)
+        rest(std::true_type{});
+      else
+        rest(std::false_type{});
+      if (chi < 0) chi = count_ge(cv, hi);
+      emit_fill(cv, [&ci](int s) { return ci[s]; }, lo, hi, k, chi, out);
+      return;
+    }
+  }
+  if (chi < 0) chi = count_ge(v, hi);
+  emit_fill(v, [lane](int s) { return s * kWave + lane; }, lo, hi, k, chi, out);
+}
+
 // Full-row search when the first count missed the candidate window: Newton
 // steps on the whole row (compacting as soon as a count lands in (k, W]),
 // then order-key bisection on the whole row, preceded by snaps for some row
@@ -718,7 +756,7 @@ __device__ __forceinline__ void process_row(const float (&v)[Q],
   if constexpr (MODE != Mode::kCapped)
     exact_row<Q, FULL, QC>(v, a, lane, scratch, out);
   else
-    capped_row<Q, FULL>(v, a, lane, out);
+    capped_row<Q, FULL, QC>(v, a, lane, scratch, out);
 }
 
 // Rows each wave keeps in flight (rows_in_flight in rtopk_internal.h): a
@@ -746,7 +784,7 @@ template <int Q, bool FULL, Mode MODE, int QC, typename IdxT>
 __global__ __launch_bounds__(kBlock) void rows_in_registers(SelectArgs a) {
   // Per wave: the LDS staging area of the exact search, (value, column)
   // pairs (see stage_entries).
-  constexpr int kScratch = (MODE != Mode::kCapped && QC > 0) ? 2 * stage_entries<Q, QC>() : 1;
+  constexpr int kScratch = QC > 0 ? 2 * stage_entries<Q, QC>() : 1;
   constexpr int D = prefetch_depth<Q>();
   // MaxK forward: the wave's LDS copy of the dense row (64*Q words) and one
   // spare word per lane.
@@ -856,7 +894,7 @@ RowsKernel any_kernel(Mode mode, int qc) {
     if constexpr (bucket_supported(Q)) return exact_kernel<Q, FULL, Mode::kBucket, IdxT>(qc);
     return nullptr;
   }
-  return rows_in_registers<Q, FULL, Mode::kCapped, 0, IdxT>;
+  return exact_kernel<Q, FULL, Mode::kCapped, IdxT>(qc);
 }
 
 }  // namespace rows_detail
