@@ -120,7 +120,9 @@ hipError_t launch_select(const SelectArgs& args, Mode mode, bool u8_index,
   SelectArgs a = args;
   // Candidate slots: the exact search compacts after its first count, the
   // capped one once the bracket's lower end leaves at most 64*qc elements.
-  const int qc = candidate_slots(slot_bucket(a.m), a.k);
+  const int q = slot_bucket(a.m);
+  const int qc = mode == Mode::kCapped ? capped_candidate_slots(q, a.k)
+                                       : candidate_slots(q, a.k);
   if (mode != Mode::kCapped) exact_model(a, qc);
   const RowsKernel fn = kernel_for(a.m, mode, u8_index, qc);
   if (fn == nullptr) return hipErrorInvalidValue;
@@ -131,7 +133,6 @@ hipError_t launch_select(const SelectArgs& args, Mode mode, bool u8_index,
   // Short rows: one group per wave, a grid over the whole matrix (waves exit
   // after their group). Long rows: a persistent grid of what fits on the
   // device at once.
-  const int q = slot_bucket(a.m);
   const int64_t d = rows_in_flight(q);
   const int64_t per_block = kWavesPerBlock * d;
   const int64_t blocks_needed = (a.n + per_block - 1) / per_block;
