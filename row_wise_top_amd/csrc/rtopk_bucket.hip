@@ -64,8 +64,12 @@ __device__ __forceinline__ void shift_in_eq(uint32_t& acc, float x, float t) {
 // LDS: a lane's 16-byte loads at a 128-byte stride would make every load
 // instruction touch 64 lines (measured: a load-only version of the kernel
 // ran at 95 us for 262,144 x 256 in 8 buckets, against 54 us with 16
-// columns). The wave instead reads its buckets as one contiguous stretch
-// and each lane takes its bucket from LDS.
+// columns). The wave instead reads its buckets with each load instruction
+// covering W * 4 contiguous bytes of 256 / W buckets, into LDS, and each
+// lane takes its bucket from there. (Staging a 64-column bucket in two
+// rounds of 32, at 9 KB of LDS per wave instead of 17 KB and twice the
+// occupancy, measured slower: 167 against 108 us, the survivors then being
+// read back from memory rather than LDS.)
 template <int W, bool VEC>
 constexpr bool lane_stage() {
   return VEC && W >= 32;
@@ -101,18 +105,18 @@ __global__ __launch_bounds__((lane_waves<W, VEC>() * kWave)) void bucket_lanes(S
   float v[W];
   u32x4* stage = stage_all[kStage ? wave_in_block : 0];
   if constexpr (kStage) {
-    // Chunk c (16 bytes, c = 64 i + lane) of the wave's live * w floats
-    // belongs to bucket (4c) / w at place (4c) mod w (a multiple of 4: w is).
-    // The quotient through a float reciprocal is exact here: 4c < 4096 and
-    // (4c + 1/2) / w stays at least 1/(2w) away from an integer.
-    const float inv_w = 1.0f / static_cast<float>(w);
-    const int floats = live * w;
+    // Chunk c = 64 i + lane (16 bytes) is place 4 (c mod (W/4)) of bucket
+    // c / (W/4). Chunks past the bucket (w is a multiple of 4) or past the
+    // buckets the wave has are not written; those places are never read as
+    // part of a bucket.
+    constexpr int kChunks = W / 4;  // chunks per bucket
 #pragma unroll
     for (int i = 0; i < W / 4; ++i) {
-      const int f = 4 * (i * kWave + lane);
-      const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(rx, f * 4, 0, kLoadPolicy);
-      const int bkt = static_cast<int>((static_cast<float>(f) + 0.5f) * inv_w);
-      if (f < floats) stage[(bkt * kStride + (f - bkt * w)) / 4] = q;
+      const int c = i * kWave + lane;
+      const int bkt = c / kChunks;
+      const int p = 4 * (c % kChunks);
+      const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(rx, (bkt * w + p) * 4, 0, kLoadPolicy);
+      if (p < w && bkt < live) stage[(bkt * kStride + p) / 4] = q;
     }
     // LDS operations of one wave complete in issue order; the barrier keeps
     // the compiler from moving the reads above the writes.
