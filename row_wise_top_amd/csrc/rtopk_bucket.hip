@@ -11,10 +11,9 @@
 // (value, column) pairs, strictly greater values moving up so that among
 // equal values the earlier column stays ahead. More: the kb largest values
 // by median-of-three insertion, then one pass in column order that keeps
-// every element above the kb-th largest value and the first few equal to it. A wave takes 64 consecutive buckets, so its
-// loads and stores cover one contiguous stretch of the input and of the
-// outputs; a lane reads its bucket with 16-byte loads where the layout
-// allows, and the lines a wave's loads share arrive once.
+// every element above the kb-th largest value and the first few equal to
+// it. A wave takes 64 consecutive buckets, so its loads and stores cover
+// one contiguous stretch of the input and of the outputs.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -64,9 +63,9 @@ __device__ __forceinline__ void shift_in_eq(uint32_t& acc, float x, float t) {
 // LDS: a lane's 16-byte loads at a 128-byte stride would make every load
 // instruction touch 64 lines (measured: a load-only version of the kernel
 // ran at 95 us for 262,144 x 256 in 8 buckets, against 54 us with 16
-// columns). The wave instead reads its buckets with each load instruction
-// covering W * 4 contiguous bytes of 256 / W buckets, into LDS, and each
-// lane takes its bucket from there. (Staging a 64-column bucket in two
+// columns). The wave instead reads its buckets into LDS with each load
+// instruction covering 1 KB of consecutive buckets (256 / W of them), and
+// each lane takes its bucket from there. (Staging a 64-column bucket in two
 // rounds of 32, at 9 KB of LDS per wave instead of 17 KB and twice the
 // occupancy, measured slower: 167 against 108 us, the survivors then being
 // read back from memory rather than LDS.)
@@ -141,7 +140,8 @@ __global__ __launch_bounds__((lane_waves<W, VEC>() * kWave)) void bucket_lanes(S
   } else {
 #pragma unroll
     for (int j = 0; j < W; ++j)
-      v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, base + j * 4, 0, kLoadPolicy));
+      v[j] = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(rx, base + j * 4, 0, kLoadPolicy));
   }
   // Places past w hold the next bucket's elements: -inf takes them out of
   // every comparison below (the inputs are finite).
