@@ -111,6 +111,9 @@ void exact_model(SelectArgs& a, int qc) {
   const double inv_sqrt_m = 1.0 / std::sqrt(m);
   a.z_first = static_cast<float>(z_first * inv_sqrt_m);
   a.half_step = static_cast<float>(0.5 / (m * normal_density(z_k)) * inv_sqrt_m);
+  a.z_first_c = static_cast<float>(z_first);
+  a.half_step_c = static_cast<float>(0.5 / (m * normal_density(z_k)));
+  a.inv_m = static_cast<float>(1.0 / m);
 }
 
 }  // namespace

@@ -37,6 +37,11 @@ struct SelectArgs {
   float half_step;   // Newton step per doubled count = r * half_step
   float* dense;      // Mode::kMaxk only: [n, m] output, survivors kept, rest 0
   int32_t buckets;   // Mode::kBucket only: buckets per input row (>= 1)
+  // Exact search, second try for rows whose first count misses: the same
+  // model on the row's mean and standard deviation sd.
+  float z_first_c;   // threshold = mean + sd * z_first_c
+  float half_step_c; // Newton step per doubled count = sd * half_step_c
+  float inv_m;       // 1 / m
 };
 
 using RowsKernel = void (*)(SelectArgs);

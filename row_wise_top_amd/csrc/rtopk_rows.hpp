@@ -742,6 +742,54 @@ __device__ __forceinline__ void exact_row(const float (&vin)[Q],
     emit_ge(v, [lane](int s) { return s * kWave + lane; }, t, out);
     return;
   }
+  // The first count missed the window: the row is not centred near zero, or
+  // not shaped like a normal sample. One retry with the row's own mean and
+  // standard deviation (shifted, one-sided or uniform rows then land in the
+  // window; measured at 262,144 x 256: N(0,1) + 1000 300 -> 62 us, -(U(0,1)
+  // + 5) 260 -> 80 us, U(0,1) 187 -> 79 us). Computing them for every row
+  // instead cost 5% on N(0,1) rows, where 99.5% of first counts land.
+  // The model only steers: sums that overflow or cancel to NaN are
+  // replaced by values that keep every threshold finite (|mean| <= 1e37,
+  // sd <= 1e33; a step then moves by at most (2m + 1) h <= ~1.5e36 and
+  // there are at most 9 of them, so |t| < 3e37).
+  {
+    auto finite_or = [](float x, float y) {
+      return (__float_as_uint(x) & 0x7f800000u) != 0x7f800000u ? x : y;
+    };
+    float s1 = 0.0f;
+#pragma unroll
+    for (int s = 0; s < Q; ++s) s1 += FULL ? v[s] : finite_or(v[s], 0.0f);  // tail: -inf
+    s1 = wave_sum(s1);
+    const float mean = fminf(fmaxf(finite_or(s1 * a.inv_m, 0.0f), -1.0e37f), 1.0e37f);
+    const float var = finite_or(fmaf(-mean, mean, s2 * a.inv_m), 1.0e38f);
+    const float sd = fminf(__builtin_amdgcn_sqrtf(fmaxf(var, 0.0f)), 1.0e33f);
+    const float h1 = sd * a.half_step_c;
+    const float t1 = fmaf(sd, a.z_first_c, mean);
+    int c1;
+    if constexpr (QC > 0) {
+      c1 = count_and_stage<Q, QC>(v, t1, lane, scratch);
+      if (static_cast<uint32_t>(c1 - k - 1) < static_cast<uint32_t>(kWave * QC - k)) {
+        float cv[QC];
+        int ci[QC];
+        read_candidates<Q, QC>(scratch, c1, lane, cv, ci);
+        exact_candidates<QC>(cv, ci, k, t1, c1, h1, out);
+        return;
+      }
+    } else {
+      c1 = count_ge(v, t1);
+    }
+    if (c1 == k) {
+      emit_ge(v, [lane](int s) { return s * kWave + lane; }, t1, out);
+      return;
+    }
+    // Carry on from whichever count came nearer to the window's middle.
+    const int mid2 = QC > 0 ? k + kWave * QC : 2 * k + 1;  // twice the middle
+    const bool second = abs(2 * c1 - mid2) < abs(2 * c - mid2);
+    if (second) {
+      exact_row_search<Q, QC>(v, k, lane, t1, c1, h1, scratch, out);
+      return;
+    }
+  }
   exact_row_search<Q, QC>(v, k, lane, t, c, h, scratch, out);
 }
 
