@@ -168,6 +168,31 @@ def test_adversarial_rows(m):
                 check(x, k, "capped", mi, eps, u8=True, label=f"adv M={m}")
 
 
+# Value distributions away from the zero-centred normal rows the threshold
+# model is tuned for: the first count then misses its window and the search
+# retries with the row's mean and standard deviation, or falls back further
+# (Newton steps, snaps, key bisection). The result must not change.
+DISTRIBUTIONS = {
+    "uniform01": lambda r, n, m: r.random((n, m)),
+    "shift1000": lambda r, n, m: r.standard_normal((n, m)) + 1000.0,
+    "negative": lambda r, n, m: -r.random((n, m)) - 5.0,
+    "lognormal2": lambda r, n, m: np.exp(2.0 * r.standard_normal((n, m))),
+    "relu": lambda r, n, m: np.maximum(r.standard_normal((n, m)), 0.0),
+    "huge_offset": lambda r, n, m: r.standard_normal((n, m)) * 1e-3 + 3e30,
+}
+
+
+@pytest.mark.parametrize("dist", sorted(DISTRIBUTIONS))
+@pytest.mark.parametrize("m,k", [(256, 32), (1000, 40), (4096, 64)])
+def test_other_value_distributions(dist, m, k):
+    rng = np.random.default_rng(900 + m)
+    x = DISTRIBUTIONS[dist](rng, 1500, m).astype(np.float32) + np.float32(0.0)
+    check(x, k, "exact", label=f"{dist} exact")
+    check(x, k, "capped", 5, 0.0, label=f"{dist} capped")
+    if m <= 256:
+        check(x, k, "exact", u8=True, label=f"{dist} exact u8")
+
+
 @pytest.mark.parametrize("n", [1, 2, 3, 5, 7, 1023, 4097, 30001])
 def test_ragged_row_counts(n):
     m = 256 if n < 30000 else 100
