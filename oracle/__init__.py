@@ -86,6 +86,8 @@ def _load():
     lib.oracle_sspmm.restype = ctypes.c_int
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_threads.restype = None
     _lib = lib
     return lib
 
@@ -231,3 +233,10 @@ def sspmm(row_ptr, col_idx, val, dy, sp_index, return_absum: bool = False):
 def threads() -> int:
     """Threads the oracle's parallel loops use (OpenMP over rows)."""
     return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Run the oracle's later calls on n threads (n >= 1)."""
+    if n < 1:
+        raise ValueError("set_threads: n must be at least 1")
+    _load().oracle_set_threads(int(n))

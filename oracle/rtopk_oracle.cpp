@@ -350,6 +350,15 @@ int oracle_maxk_backward(const float* grad_sp, const int32_t* sp_index,
 }
 
 // Number of threads a parallel region of this library uses.
+// Sets the number of threads later calls use (n >= 1); a no-op without OpenMP.
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int oracle_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

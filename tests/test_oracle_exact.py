@@ -82,3 +82,21 @@ def test_rejects_bad_arguments():
         oracle.exact(x, 0)
     with pytest.raises(ValueError):
         oracle.exact(x, 5)
+
+
+def test_thread_count_does_not_change_results():
+    # The baseline timing runs the oracle on all host threads and on one.
+    x = workloads.normal(3000, 256, 17)
+    before = oracle.threads()
+    want = oracle.exact(x, 32)
+    oracle.set_threads(1)
+    try:
+        assert oracle.threads() == 1
+        got = oracle.exact(x, 32)
+    finally:
+        oracle.set_threads(before)
+    assert oracle.threads() == before
+    assert np.array_equal(got[1], want[1])
+    assert np.array_equal(got[0].view(np.uint32), want[0].view(np.uint32))
+    with pytest.raises(ValueError):
+        oracle.set_threads(0)
