@@ -416,29 +416,53 @@ def main():
             sp_np = (feats[0][0].cpu().numpy(), feats[0][1].cpu().numpy().astype(np.int32))
         if args.op == "sspmm":
             dy_np = dys[0].cpu().numpy()
-        passes, t_cpu = 0, 0.0
-        while t_cpu < args.cpu_seconds and passes < 100:
-            t = time.perf_counter()
+
+        def oracle_pass(r):
+            """The op on the first r rows of the batch (r = n: all of it)."""
             if args.op == "maxk_backward":
-                oracle.maxk_backward(g_np, i_np, m)
+                oracle.maxk_backward(g_np[:r], i_np[:r], m)
             elif args.op == "maxk_forward":
-                oracle.maxk_forward(x_np, k)
+                oracle.maxk_forward(x_np[:r], k)
             elif args.op == "bucketed":
-                oracle.bucketed(x_np, k, args.buckets)
+                oracle.bucketed(x_np[:r], k, args.buckets)
             elif args.op == "spgemm":
-                oracle.spgemm(rp_np, ci_np, va_np, n, sp_np[0], sp_np[1], m)
+                e = int(rp_np[r])
+                oracle.spgemm(rp_np[:r + 1], ci_np[:e], va_np[:e], n, sp_np[0], sp_np[1], m)
             elif args.op == "sspmm":
-                oracle.sspmm(rp_np, ci_np, va_np, dy_np, sp_np[1])
+                e = int(rp_np[r])
+                oracle.sspmm(rp_np[:r + 1], ci_np[:e], va_np[:e], dy_np[:r], sp_np[1])
             elif args.mode == "exact":
-                oracle.exact(x_np, k)
+                oracle.exact(x_np[:r], k)
             else:
-                oracle.capped(x_np, k, args.max_iter, args.eps)
-            t_cpu += time.perf_counter() - t
-            passes += 1
+                oracle.capped(x_np[:r], k, args.max_iter, args.eps)
+
+        def timed_passes(r, seconds):
+            passes, spent = 0, 0.0
+            while spent < seconds and passes < 100:
+                t = time.perf_counter()
+                oracle_pass(r)
+                spent += time.perf_counter() - t
+                passes += 1
+            return passes, spent
+
+        cores = oracle.threads()
+        passes, t_cpu = timed_passes(n, args.cpu_seconds)
         cpu = {"value": passes * n / t_cpu, "unit": "rows/s",
-               "cores": oracle.threads(), "kind": "oracle",
+               "cores": cores, "kind": "oracle",
                "sample": f"{passes} full pass(es) over the same {n}-row batch "
                          f"({t_cpu:.1f} s of oracle time)"}
+        # The same oracle on one thread, over the first rows of the batch (a
+        # slice that one thread finishes in about two seconds).
+        per_row_1t = t_cpu / (passes * n) * cores
+        r1 = int(min(n, max(1024, 2.0 / per_row_1t)))
+        oracle.set_threads(1)
+        try:
+            p1, t1 = timed_passes(r1, max(2.0, args.cpu_seconds / 4))
+        finally:
+            oracle.set_threads(cores)
+        cpu["single_thread"] = {"value": p1 * r1 / t1, "unit": "rows/s", "cores": 1,
+                                "sample": f"{p1} pass(es) over the first {r1} rows "
+                                          f"({t1:.1f} s of oracle time)"}
 
     line = {
         "metric": (METRIC if args.op == "select" else
