@@ -13,7 +13,7 @@
 namespace rtopk {
 
 // Resident blocks per CU for a kernel on a device, cached per device.
-int resident_blocks(const void* fn, int device) {
+int resident_blocks(const void* fn, int threads, int device) {
   static std::mutex mu;
   static std::unordered_map<const void*, int> cache[64];
   std::lock_guard<std::mutex> lock(mu);
@@ -21,7 +21,7 @@ int resident_blocks(const void* fn, int device) {
   auto it = c.find(fn);
   if (it != c.end()) return it->second;
   int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, kBlock, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, threads, 0) !=
           hipSuccess ||
       blocks < 1)
     blocks = 1;
@@ -132,21 +132,22 @@ hipError_t launch_select(const SelectArgs& args, Mode mode, bool u8_index,
   int device = 0;
   hipError_t err = hipGetDevice(&device);
   if (err != hipSuccess) return err;
-  // One wave per row at a time, in groups of D = rows_in_flight(q) rows.
+  // One wave per row at a time, in groups of D = rows_in_flight(q, .) rows.
   // Short rows: one group per wave, a grid over the whole matrix (waves exit
   // after their group). Long rows: a persistent grid of what fits on the
   // device at once.
-  const int64_t d = rows_in_flight(q);
-  const int64_t per_block = kWavesPerBlock * d;
+  const int64_t d = rows_in_flight(q, mode == Mode::kMaxk);
+  const int threads = kWave * row_waves(q);
+  const int64_t per_block = row_waves(q) * d;
   const int64_t blocks_needed = (a.n + per_block - 1) / per_block;
   int64_t grid = blocks_needed;
   if (!one_group_per_wave(q) || blocks_needed > 0x7fffffff) {
     const int64_t resident =
         static_cast<int64_t>(cu_count(device)) *
-        resident_blocks(reinterpret_cast<const void*>(fn), device);
+        resident_blocks(reinterpret_cast<const void*>(fn), threads, device);
     grid = blocks_needed < resident ? blocks_needed : resident;
   }
-  hipLaunchKernelGGL(fn, dim3(static_cast<uint32_t>(grid)), dim3(kBlock), 0,
+  hipLaunchKernelGGL(fn, dim3(static_cast<uint32_t>(grid)), dim3(threads), 0,
                      stream, a);
   return hipGetLastError();
 }

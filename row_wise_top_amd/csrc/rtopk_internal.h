@@ -14,6 +14,11 @@ constexpr int kMaxRowLength = 8192;
 constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = kWave * kWavesPerBlock;
+// Waves per block of the one-wave-per-row selection kernels, by slots per
+// lane q: single-wave blocks for rows of at most 512 columns (a wave's slot
+// on the CU frees as soon as it ends, not when the slowest of its block
+// does), four waves for longer rows.
+constexpr int row_waves(int q) { return q <= 8 ? 1 : 4; }
 
 // kMaxk: the exact search, plus the dense [n, m] MaxK output (SelectArgs::dense).
 // kBucket: the exact search on buckets: each kernel row is one bucket of an
@@ -47,12 +52,16 @@ struct SelectArgs {
 using RowsKernel = void (*)(SelectArgs);
 
 // Rows a wave of the selection kernel keeps in flight for q slots per lane:
-// the row being worked on plus rows_in_flight(q) - 1 whose loads are
-// issued. Short rows (q <= 16) are also the rows each wave takes in all: the
-// grid then covers the matrix once (a wave that loads its rows first and
-// stores last never waits on its own stores, which share the load counter
-// on this GPU). Longer rows get no prefetch and a persistent grid.
-constexpr int rows_in_flight(int q) { return q <= 4 ? 4 : (q <= 16 ? 2 : 1); }
+// the row being worked on plus rows_in_flight(q, dense) - 1 whose loads are
+// issued. About 4 KB of a wave's rows are in flight for rows of at most 384
+// columns; the fused MaxK forward (dense: it also writes each row back
+// whole) keeps two. Short rows (q <= 16) are also the rows each wave takes
+// in all: the grid then covers the matrix once (a wave that loads its rows
+// first and stores last never waits on its own stores, which share the load
+// counter on this GPU). Longer rows get no prefetch and a persistent grid.
+constexpr int rows_in_flight(int q, bool dense) {
+  return q > 16 ? 1 : dense ? 2 : q <= 2 ? 8 : q <= 6 ? 4 : 2;
+}
 constexpr bool one_group_per_wave(int q) { return q <= 16; }
 
 // Rows the fused MaxK forward kernel takes (its LDS holds the dense row);
@@ -93,9 +102,9 @@ inline int capped_candidate_slots(int q, int k) {
   return 0;
 }
 
-// Resident blocks per CU of `fn` launched with kBlock threads on `device`,
-// and the device's CU count (both cached per device).
-int resident_blocks(const void* fn, int device);
+// Resident blocks per CU of `fn` launched with `threads` threads per block on
+// `device`, and the device's CU count (both cached per device).
+int resident_blocks(const void* fn, int threads, int device);
 int cu_count(int device);
 
 // MaxK backward (and compressed rows to dense): out[r, idx[r, i]] = src[r, i]

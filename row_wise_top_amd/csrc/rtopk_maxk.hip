@@ -261,7 +261,7 @@ hipError_t launch_scatter(const ScatterArgs& a, bool u8_index,
     // The chunked kernel loops over rows: a persistent grid.
     const int64_t resident =
         static_cast<int64_t>(cu_count(device)) *
-        resident_blocks(reinterpret_cast<const void*>(fn), device);
+        resident_blocks(reinterpret_cast<const void*>(fn), kBlock, device);
     grid = blocks_needed < resident ? blocks_needed : resident;
   }
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;

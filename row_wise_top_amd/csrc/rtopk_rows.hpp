@@ -809,11 +809,10 @@ __device__ __forceinline__ void process_row(const float (&v)[Q],
 
 // Rows each wave keeps in flight (rows_in_flight in rtopk_internal.h): a
 // group of D consecutive rows whose loads are all issued before the first
-// of them is worked on. Four rows for rows of at most 256 (measured faster
-// than two or three; 39 VGPRs keep 8 waves per SIMD).
-template <int Q>
+// of them is worked on.
+template <int Q, Mode MODE>
 constexpr int prefetch_depth() {
-  return rows_in_flight(Q);
+  return rows_in_flight(Q, MODE == Mode::kMaxk);
 }
 
 // Row order. Wave w of S works through groups of D consecutive rows:
@@ -829,26 +828,27 @@ constexpr int prefetch_depth() {
 // of the matrix re-read the last row (the loads stay unconditional and the
 // compiler's wait counts exact) and are not processed.
 template <int Q, bool FULL, Mode MODE, int QC, typename IdxT>
-__global__ __launch_bounds__(kBlock) void rows_in_registers(SelectArgs a) {
+__global__ __launch_bounds__(kWave * row_waves(Q)) void rows_in_registers(SelectArgs a) {
   // Per wave: the LDS staging area of the exact search, (value, column)
   // pairs (see stage_entries).
   constexpr int kScratch = QC > 0 ? 2 * stage_entries<Q, QC>() : 1;
-  constexpr int D = prefetch_depth<Q>();
+  constexpr int D = prefetch_depth<Q, MODE>();
+  constexpr int kRowWaves = row_waves(Q);
   // MaxK forward: the wave's LDS copy of the dense row (64*Q words) and one
   // spare word per lane.
   constexpr bool kDense = MODE == Mode::kMaxk;
   constexpr int kDenseWords = kDense ? kWave * (Q + 1) : 1;
   constexpr bool kBuckets = MODE == Mode::kBucket;
-  __shared__ uint32_t scratch_all[kWavesPerBlock][kScratch];
-  __shared__ uint32_t dense_all[kWavesPerBlock][kDenseWords];
+  __shared__ uint32_t scratch_all[kRowWaves][kScratch];
+  __shared__ uint32_t dense_all[kRowWaves][kDenseWords];
   const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
   const int wave_in_block =
       __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   uint32_t* scratch = scratch_all[wave_in_block];
   uint32_t* dense = dense_all[wave_in_block];
   const uint32_t spare = static_cast<uint32_t>(kWave * Q + lane);
-  const int64_t waves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
-  const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_in_block;
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * kRowWaves;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * kRowWaves + wave_in_block;
   const int64_t stride = waves * D;
 #pragma unroll 1
   for (int64_t r = w * D; r < a.n; r += stride) {
