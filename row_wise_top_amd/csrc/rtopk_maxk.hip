@@ -76,6 +76,10 @@ __device__ __forceinline__ void store_row(const u32x4* buf4, float* dst,
 // then use 128 KB of the 160 KB.
 constexpr int kBatchFloats = 1024;
 
+// Waves per block of the scatter kernels.
+constexpr int kScatterWaves = 4;
+constexpr int kScatterBlock = kWave * kScatterWaves;
+
 // Rows of length m <= 256*S, in batches of B consecutive rows,
 // B = min(kBatchFloats / (256*S), 64*EB / k) >= 1 (host checked). One wave
 // takes one batch and exits: it loads the batch's B*k entries (contiguous in
@@ -90,16 +94,16 @@ constexpr int kBatchFloats = 1024;
 // waves streaming (measured at the 262,144 x 256 shape: 63.8 us for the
 // persistent loop, about 20% less one-shot).
 template <typename IdxT, int S, int EB, bool VEC>
-__global__ __launch_bounds__(kBlock) void scatter_rows(ScatterArgs a, int B) {
+__global__ __launch_bounds__(kScatterBlock) void scatter_rows(ScatterArgs a, int B) {
   constexpr int kPad = 256 * S;                     // LDS row stride (floats)
   constexpr int kMaxB = kBatchFloats / kPad;        // rows the LDS area holds
-  __shared__ u32x4 lds[kWavesPerBlock][kBatchFloats / 4];
+  __shared__ u32x4 lds[kScatterWaves][kBatchFloats / 4];
   const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
   const int wave_in_block =
       __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   u32x4* buf4 = lds[wave_in_block];
   uint32_t* buf = reinterpret_cast<uint32_t*>(buf4);
-  const int64_t j = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_in_block;
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * kScatterWaves + wave_in_block;
   const int64_t row0 = j * B;
   if (row0 >= a.n) return;
   const int m = a.m, k = a.k;
@@ -162,16 +166,16 @@ __global__ __launch_bounds__(kBlock) void scatter_rows(ScatterArgs a, int B) {
 template <typename IdxT, bool VEC>
 __device__ __forceinline__ void scatter_rows_chunked_body(const ScatterArgs& a) {
   constexpr int S = kChunk / 256;
-  __shared__ u32x4 lds[kWavesPerBlock][S * kWave];
+  __shared__ u32x4 lds[kScatterWaves][S * kWave];
   const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
   const int wave_in_block =
       __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   u32x4* buf4 = lds[wave_in_block];
   uint32_t* buf = reinterpret_cast<uint32_t*>(buf4);
-  const int64_t waves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * kScatterWaves;
   const int m = a.m, k = a.k;
   const IdxT* idx = static_cast<const IdxT*>(a.idx);
-  for (int64_t r = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_in_block;
+  for (int64_t r = static_cast<int64_t>(blockIdx.x) * kScatterWaves + wave_in_block;
        r < a.n; r += waves) {
     const float* s = a.src + r * k;
     const IdxT* q = idx + r * k;
@@ -196,7 +200,7 @@ using ScatterKernel = void (*)(ScatterArgs, int);
 constexpr int bucket124(int v) { return v <= 1 ? 1 : (v <= 2 ? 2 : 4); }
 
 template <typename IdxT, bool VEC>
-__global__ __launch_bounds__(kBlock) void scatter_rows_chunked_entry(ScatterArgs a, int) {
+__global__ __launch_bounds__(kScatterBlock) void scatter_rows_chunked_entry(ScatterArgs a, int) {
   scatter_rows_chunked_body<IdxT, VEC>(a);
 }
 
@@ -255,17 +259,17 @@ hipError_t launch_scatter(const ScatterArgs& a, bool u8_index,
   hipError_t err = hipGetDevice(&device);
   if (err != hipSuccess) return err;
   const int64_t batches = (a.n + rows_per_batch - 1) / rows_per_batch;
-  const int64_t blocks_needed = (batches + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t blocks_needed = (batches + kScatterWaves - 1) / kScatterWaves;
   int64_t grid = blocks_needed;
   if (chunked) {
     // The chunked kernel loops over rows: a persistent grid.
     const int64_t resident =
         static_cast<int64_t>(cu_count(device)) *
-        resident_blocks(reinterpret_cast<const void*>(fn), kBlock, device);
+        resident_blocks(reinterpret_cast<const void*>(fn), kScatterBlock, device);
     grid = blocks_needed < resident ? blocks_needed : resident;
   }
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(fn, dim3(static_cast<uint32_t>(grid)), dim3(kBlock), 0,
+  hipLaunchKernelGGL(fn, dim3(static_cast<uint32_t>(grid)), dim3(kScatterBlock), 0,
                      stream, a, rows_per_batch);
   return hipGetLastError();
 }
