@@ -445,7 +445,8 @@ def main():
                 passes += 1
             return passes, spent
 
-        cores = oracle.threads()
+        # The oracle's SSpMM scatters into one accumulator on one thread.
+        cores = 1 if args.op == "sspmm" else oracle.threads()
         passes, t_cpu = timed_passes(n, args.cpu_seconds)
         cpu = {"value": passes * n / t_cpu, "unit": "rows/s",
                "cores": cores, "kind": "oracle",
@@ -453,16 +454,20 @@ def main():
                          f"({t_cpu:.1f} s of oracle time)"}
         # The same oracle on one thread, over the first rows of the batch (a
         # slice that one thread finishes in about two seconds).
-        per_row_1t = t_cpu / (passes * n) * cores
-        r1 = int(min(n, max(1024, 2.0 / per_row_1t)))
-        oracle.set_threads(1)
-        try:
-            p1, t1 = timed_passes(r1, max(2.0, args.cpu_seconds / 4))
-        finally:
-            oracle.set_threads(cores)
-        cpu["single_thread"] = {"value": p1 * r1 / t1, "unit": "rows/s", "cores": 1,
-                                "sample": f"{p1} pass(es) over the first {r1} rows "
-                                          f"({t1:.1f} s of oracle time)"}
+        if cores == 1:
+            cpu["single_thread"] = dict(cpu, sample="the figure above (one thread)")
+            del cpu["single_thread"]["kind"]
+        else:
+            per_row_1t = t_cpu / (passes * n) * cores
+            r1 = int(min(n, max(1024, 2.0 / per_row_1t)))
+            oracle.set_threads(1)
+            try:
+                p1, t1 = timed_passes(r1, max(2.0, args.cpu_seconds / 4))
+            finally:
+                oracle.set_threads(cores)
+            cpu["single_thread"] = {"value": p1 * r1 / t1, "unit": "rows/s", "cores": 1,
+                                    "sample": f"{p1} pass(es) over the first {r1} rows "
+                                              f"({t1:.1f} s of oracle time)"}
 
     line = {
         "metric": (METRIC if args.op == "select" else
