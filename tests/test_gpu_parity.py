@@ -219,6 +219,27 @@ def test_random_shapes_ties_and_scales():
         check(x, k, "exact", label=f"rand{t}")
         check(x, k, "capped", int(rng.integers(-1, 12)), float(rng.choice([0.0, 1e-3, 0.25])),
               label=f"rand{t}")
+        if m <= 256:
+            check(x, k, "exact", u8=True, label=f"rand{t} u8")
+
+
+def test_random_long_rows():
+    # Rows of 1,400 to 8,192 columns (16 to 128 slots per lane, full and
+    # partial last slots, four-wave blocks), row counts spanning several
+    # waves and a partial last block.
+    rng = np.random.default_rng(77)
+    for t in range(12):
+        m = int(rng.integers(1400, 8193))
+        n = int(rng.integers(1, 70))
+        k = int(rng.integers(1, min(m, 512) + 1))
+        if t % 3 == 0:
+            x = rng.standard_normal((n, m)).astype(np.float32)
+        elif t % 3 == 1:
+            x = (np.round(rng.standard_normal((n, m)) * 4) / 4).astype(np.float32) + np.float32(0)
+        else:
+            x = (rng.standard_normal((n, m)) * 3 + 50).astype(np.float32)
+        check(x, k, "exact", label=f"long{t}")
+        check(x, k, "capped", int(rng.integers(-1, 10)), 0.0, label=f"long{t}")
 
 
 def test_outputs_untouched_outside_bounds_and_deterministic():
