@@ -449,6 +449,7 @@ def main():
         cores = 1 if args.op == "sspmm" else oracle.threads()
         passes, t_cpu = timed_passes(n, args.cpu_seconds)
         cpu = {"value": passes * n / t_cpu, "unit": "rows/s",
+               "gbs": passes * n * per_row / t_cpu / 1e9,
                "cores": cores, "kind": "oracle",
                "sample": f"{passes} full pass(es) over the same {n}-row batch "
                          f"({t_cpu:.1f} s of oracle time)"}
@@ -465,7 +466,8 @@ def main():
                 p1, t1 = timed_passes(r1, max(2.0, args.cpu_seconds / 4))
             finally:
                 oracle.set_threads(cores)
-            cpu["single_thread"] = {"value": p1 * r1 / t1, "unit": "rows/s", "cores": 1,
+            cpu["single_thread"] = {"value": p1 * r1 / t1, "unit": "rows/s",
+                                    "gbs": p1 * r1 * per_row / t1 / 1e9, "cores": 1,
                                     "sample": f"{p1} pass(es) over the first {r1} rows "
                                               f"({t1:.1f} s of oracle time)"}
 
