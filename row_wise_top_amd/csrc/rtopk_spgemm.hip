@@ -13,7 +13,7 @@
 // pair, up to 4 edges per instruction, see accumulate), then flushed:
 //  * a row wholly inside the wave's range is stored once;
 //  * a row cut by a range boundary is added to Y with float atomics; such
-//    rows are zeroed first by a small kernel (one wave per boundary).
+//    rows are zeroed first by a small kernel (one lane per row).
 // Every wave does about the same number of edges whatever the degree
 // distribution, and each complete row still reaches HBM exactly once.
 //
@@ -60,22 +60,31 @@ __device__ __forceinline__ int64_t clamp_edge(int64_t e, int64_t nnz) {
 }
 
 // Zero Y[i, :] for every row i cut by an interior range boundary
-// p = w * C (w >= 1): row_ptr[i] < p < row_ptr[i + 1].
+// p = w * C (w >= 1): start < p < end. The smallest multiple of C above
+// start is (start / C + 1) * C, so the row is cut iff that lies below end.
+// One lane per row reads its two offsets (coalesced), then the wave clears
+// its cut rows one after another. A hub row that many boundaries cut is
+// cleared once (one wave per boundary, each first searching row_ptr for its
+// row, took 23 us on the 262,144-node graph).
 __global__ __launch_bounds__(kBlock) void zero_cut_rows(SpgemmArgs a) {
   const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
-  const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock +
-                    __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave) + 1;
-  const int64_t p = w * a.chunk;
-  if (p >= a.nnz) return;
-  const int64_t i = last_row_at_or_before(a.row_ptr, a.n_dst, p, lane);
-  if (i >= a.n_dst) return;
-  const int64_t start = a.row_ptr[i];
-  const int64_t end = a.row_ptr[i + 1];
-  if (!(start < p && p < end)) return;
-  const __amdgpu_buffer_rsrc_t ry =
-      __builtin_amdgcn_make_buffer_rsrc(a.y + i * a.m, 0, a.m * 4, kRsrcWord3);
-  for (int c = lane; c < a.m; c += kWave)
-    __builtin_amdgcn_raw_buffer_store_b32(0u, ry, c * 4, 0, 0);
+  const int64_t base =
+      static_cast<int64_t>(blockIdx.x) * kBlock +
+      __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave) * kWave;
+  const int64_t i = base + lane;
+  bool cut = false;
+  if (i < a.n_dst) {
+    const int64_t start = clamp_edge(a.row_ptr[i], a.nnz);
+    const int64_t end = clamp_edge(a.row_ptr[i + 1], a.nnz);
+    cut = (start / a.chunk + 1) * a.chunk < end;
+  }
+  for (uint64_t mask = ballot(cut); mask != 0; mask &= mask - 1) {
+    const int64_t r = base + __builtin_ctzll(mask);
+    const __amdgpu_buffer_rsrc_t ry =
+        __builtin_amdgcn_make_buffer_rsrc(a.y + r * a.m, 0, a.m * 4, kRsrcWord3);
+    for (int c = lane; c < a.m; c += kWave)
+      __builtin_amdgcn_raw_buffer_store_b32(0u, ry, c * 4, 0, 0);
+  }
 }
 
 // Accumulate edges [s0, s1) of a row into the wave's LDS accumulators. The
@@ -363,9 +372,9 @@ hipError_t launch_spgemm(SpgemmArgs a, bool u8_index, hipStream_t stream) {
   const int64_t blocks = (a.waves + a.waves_per_block - 1) / a.waves_per_block;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   // Rows cut by a range boundary start at zero.
-  const int64_t boundaries = a.waves - 1;
-  if (boundaries > 0) {
-    const int64_t zb = (boundaries + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (a.waves > 1 && a.n_dst > 0) {
+    const int64_t zb = (a.n_dst + kBlock - 1) / kBlock;
+    if (zb > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(zero_cut_rows, dim3(static_cast<uint32_t>(zb)), dim3(kBlock), 0,
                        stream, a);
     const hipError_t err = hipGetLastError();
