@@ -31,7 +31,8 @@
  *   stream   HIP stream to enqueue on; NULL means the null stream.
  * Outputs must not overlap x or each other. All pointers are owned by the
  * caller; the library allocates, frees and synchronises nothing, and keeps no
- * state between calls apart from cached device properties (re-entrant).
+ * state between calls apart from cached device properties and, per calling
+ * thread, the host-side search constants of the last (M, k) (re-entrant).
  *
  * Asynchrony. Each call validates its arguments on the host, enqueues one
  * kernel on `stream` and returns. Faults in the kernel surface at the

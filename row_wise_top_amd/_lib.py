@@ -88,16 +88,26 @@ def _prepare(x, k, out_val, out_idx, index_dtype):
         out_val = torch.empty((n, k), dtype=torch.float32, device=x.device)
     if out_idx is None:
         out_idx = torch.empty((n, k), dtype=index_dtype, device=x.device)
+    # Device indices as ints: cheaper than comparing torch.device objects on
+    # every call of a small batch.
+    dev = x.get_device()
     for t, dt in ((out_val, torch.float32), (out_idx, index_dtype)):
-        if (t.device != x.device or t.dtype != dt or not t.is_contiguous()
-                or tuple(t.shape) != (n, k)):
+        if (not t.is_cuda or t.get_device() != dev or t.dtype != dt
+                or not t.is_contiguous() or t.shape != (n, k)):
             raise ValueError(f"outputs must be contiguous [{n}, {k}] {dt} on {x.device}")
     return n, m, out_val, out_idx
 
 
 def _stream(x, stream):
+    """The HIP stream handle to enqueue on: torch's current stream of x's
+    device unless one is given (a torch stream or a raw handle)."""
     import torch
     if stream is None:
+        # The raw handle straight from torch's stream registry when this
+        # torch has the accessor (no Stream object built per call).
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            return raw(x.get_device())
         return torch.cuda.current_stream(x.device).cuda_stream
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
