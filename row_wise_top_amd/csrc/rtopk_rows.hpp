@@ -765,29 +765,41 @@ __device__ __forceinline__ void exact_row(const float (&vin)[Q],
     const float sd = fminf(__builtin_amdgcn_sqrtf(fmaxf(var, 0.0f)), 1.0e33f);
     const float h1 = sd * a.half_step_c;
     const float t1 = fmaf(sd, a.z_first_c, mean);
-    int c1;
-    if constexpr (QC > 0) {
-      c1 = count_and_stage<Q, QC>(v, t1, lane, scratch);
-      if (static_cast<uint32_t>(c1 - k - 1) < static_cast<uint32_t>(kWave * QC - k)) {
-        float cv[QC];
-        int ci[QC];
-        read_candidates<Q, QC>(scratch, c1, lane, cv, ci);
-        exact_candidates<QC>(cv, ci, k, t1, c1, h1, out);
+    // Rows of 8,192 columns: a retry threshold that moves the expected
+    // count by less than a quarter of the candidate window ((W - k) / 4
+    // elements; a step of h moves it by one half, and the smaller of the two
+    // models' steps is the scale) would count about the same elements again,
+    // as happens on rows centred near zero with many equal values whose
+    // first count jumped over the window; those carry on from the first
+    // count. On shorter rows the retry pays even then and always runs.
+    bool near = false;
+    if constexpr (QC > 0 && Q >= 128)
+      near = 2.0f * fabsf(t1 - t) < static_cast<float>(kWave * QC - k) * fminf(h, h1);
+    if (!near) {
+      int c1;
+      if constexpr (QC > 0) {
+        c1 = count_and_stage<Q, QC>(v, t1, lane, scratch);
+        if (static_cast<uint32_t>(c1 - k - 1) < static_cast<uint32_t>(kWave * QC - k)) {
+          float cv[QC];
+          int ci[QC];
+          read_candidates<Q, QC>(scratch, c1, lane, cv, ci);
+          exact_candidates<QC>(cv, ci, k, t1, c1, h1, out);
+          return;
+        }
+      } else {
+        c1 = count_ge(v, t1);
+      }
+      if (c1 == k) {
+        emit_ge(v, [lane](int s) { return s * kWave + lane; }, t1, out);
         return;
       }
-    } else {
-      c1 = count_ge(v, t1);
-    }
-    if (c1 == k) {
-      emit_ge(v, [lane](int s) { return s * kWave + lane; }, t1, out);
-      return;
-    }
-    // Carry on from whichever count came nearer to the window's middle.
-    const int mid2 = QC > 0 ? k + kWave * QC : 2 * k + 1;  // twice the middle
-    const bool second = abs(2 * c1 - mid2) < abs(2 * c - mid2);
-    if (second) {
-      exact_row_search<Q, QC>(v, k, lane, t1, c1, h1, scratch, out);
-      return;
+      // Carry on from whichever count came nearer to the window's middle.
+      const int mid2 = QC > 0 ? k + kWave * QC : 2 * k + 1;  // twice the middle
+      const bool second = abs(2 * c1 - mid2) < abs(2 * c - mid2);
+      if (second) {
+        exact_row_search<Q, QC>(v, k, lane, t1, c1, h1, scratch, out);
+        return;
+      }
     }
   }
   exact_row_search<Q, QC>(v, k, lane, t, c, h, scratch, out);
