@@ -90,16 +90,27 @@ inline int candidate_slots(int q, int k) {
   return 0;
 }
 
-// Candidate slots of the capped search: the widest window built for q slots
-// (the largest of 8, 4, 2, 1 with 2*QC <= q) that holds k, so that the
-// search compacts as early as possible (its thresholds are the specified
-// midpoints, not aimed at the window). Measured at 1,048,576 x 1,024, k = 64,
-// max_iter 2: 1,026 us with the exact search's QC = 2, 892 us with QC = 8.
-inline int capped_candidate_slots(int q, int k) {
+// Candidate slots of the capped search. Few steps (max_iter 1 to 3): the
+// widest window built for q slots (the largest of 8, 4, 2, 1 with
+// 2*QC <= q) that holds k, so that the search compacts as early as possible
+// (its thresholds are the specified midpoints, not aimed at the window).
+// More steps, or no cap: each step after the compaction costs QC compares,
+// so where the widest window is at least four times the exact search's,
+// the exact search's window. Measured at 1,048,576 x 1,024, k = 64 (QC 8
+// against 2, us): max_iter 2 897 / 1,022, 3 857 / 984, 4 855 / 840, 5 869 /
+// 838, 8 910 / 832, uncapped 935 / 839. At 262,144 x 256, k = 32 (QC 2
+// against 1) the wide window is as fast or faster at every max_iter.
+inline int capped_candidate_slots(int q, int k, int max_iter) {
+  int wide = 0;
   for (int qc : {8, 4, 2, 1}) {
-    if (2 * qc <= q && kWave * qc >= k) return qc;
+    if (2 * qc <= q && kWave * qc >= k) {
+      wide = qc;
+      break;
+    }
   }
-  return 0;
+  const int narrow = candidate_slots(q, k);
+  if ((max_iter < 0 || max_iter >= 4) && narrow > 0 && wide >= 4 * narrow) return narrow;
+  return wide;
 }
 
 // Resident blocks per CU of `fn` launched with `threads` threads per block on
