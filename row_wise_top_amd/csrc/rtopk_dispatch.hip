@@ -141,7 +141,7 @@ hipError_t launch_select(const SelectArgs& args, Mode mode, bool u8_index,
   // capped one once the bracket's lower end leaves at most 64*qc elements.
   const int q = slot_bucket(a.m);
   const int qc = mode == Mode::kCapped ? capped_candidate_slots(q, a.k, a.max_iter)
-                                       : candidate_slots(q, a.k);
+                                       : exact_candidate_slots(q, a.k);
   if (mode != Mode::kCapped) exact_model(a, qc);
   const RowsKernel fn = kernel_for(a.m, mode, u8_index, qc);
   if (fn == nullptr) return hipErrorInvalidValue;

@@ -90,6 +90,25 @@ inline int candidate_slots(int q, int k) {
   return 0;
 }
 
+// Candidate slots of the exact search: rows of 1,024 columns and more take
+// a window of 4k candidates where one is built, shorter rows one of 2k
+// (candidate_slots). The wider window lets more first counts land in it;
+// rows with many equal values gain most, since their counts jump in large
+// steps. Measured (one box, 2k against 4k window, us): 16,384 rows of
+// N(0,1) rounded to steps of 0.25, k = 64, at 1,024 / 2,048 / 4,096 / 8,192
+// columns: 19.0 / 17.8, 35.8 / 27.7, 70.2 / 52.2, 207 / 139.5; N(0,1)
+// rows: 1,048,576 x 1,024, k = 64, 831 / 824; 262,144 x 1,024, k = 32,
+// 190.6 / 187.8; 65,536 x 2,048, k = 64, 107.1 / 111.1. At 256 and 512
+// columns the 4k window was slower (headline 56.0 against 63.1).
+inline int exact_candidate_slots(int q, int k) {
+  if (q >= 16) {
+    for (int qc : {1, 2, 4, 8}) {
+      if (kWave * qc >= 4 * k && 2 * qc <= q) return qc;
+    }
+  }
+  return candidate_slots(q, k);
+}
+
 // Candidate slots of the capped search. Few steps (max_iter 1 to 3): the
 // widest window built for q slots (the largest of 8, 4, 2, 1 with
 // 2*QC <= q) that holds k, so that the search compacts as early as possible
