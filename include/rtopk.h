@@ -34,16 +34,24 @@
  * state between calls apart from cached device properties and, per calling
  * thread, the host-side search constants of the last (M, k) (re-entrant).
  *
- * Asynchrony. Each call validates its arguments on the host, enqueues one
- * kernel on `stream` and returns. Faults in the kernel surface at the
- * caller's next synchronisation, as for any HIP launch.
+ * Asynchrony. Each call validates its arguments on the host, enqueues its
+ * kernel on `stream` (two kernels, in order, for the calls that say so:
+ * rtopk_maxk_forward on rows longer than 1,024, rtopk_cbsr_spgemm and
+ * rtopk_cbsr_sspmm) and returns. Faults in a kernel surface at the caller's
+ * next synchronisation, as for any HIP launch.
  *
  * Errors. RTOPK_ERROR_INVALID_VALUE: a NULL pointer (when N > 0), N < 0,
  * M < 1, k < 1, k > M, eps < 0 or NaN (and the bucket conditions below).
  * RTOPK_ERROR_NOT_SUPPORTED: M > RTOPK_MAX_ROW_LENGTH, or a _u8 form with
- * M > 256 (and buckets longer than 1024). RTOPK_ERROR_LAUNCH:
- * the HIP runtime reported an error while enqueuing. On any error nothing is
- * enqueued and the outputs are untouched.
+ * M > 256 (and buckets longer than 1024). With either of these nothing is
+ * enqueued and the outputs are untouched: every argument and launch
+ * configuration is checked before the first launch. RTOPK_ERROR_LAUNCH: the
+ * HIP runtime reported an error while enqueuing (hipGetLastError after a
+ * launch). A one-kernel call then has enqueued nothing. A two-kernel call
+ * checks each launch before the next, so nothing follows a failed launch;
+ * but when the second launch fails, the first kernel (the selection, or the
+ * zeroing kernel of the aggregation calls) is already enqueued and the
+ * outputs are unspecified.
  */
 #ifndef RTOPK_H_
 #define RTOPK_H_

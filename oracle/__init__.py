@@ -7,7 +7,9 @@ compiled with g++ and loaded through ctypes.
 
 ``exact`` is the plain definition of row-wise top-k (RTop-K summary page,
 "Problem"/"Approach"; MaxK-GNN review, "How MaxK-GNN works": exactly k
-survivors per row), ties at the k-th value going to the lowest indices.
+survivors per row), ties at the k-th value going to the lowest indices, by
+partial selection (``std::nth_element``); ``exact_by_sort`` reaches the same
+result through a full stable sort.
 ``capped`` is the threshold search with early stopping and tie fill of the RTop-K
 summary page, "Approach", in the reading spelled out in ``rtopk_oracle.cpp``.
 Both return the survivors of each row in ascending index order.
@@ -34,33 +36,59 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "rtopk_oracle.cpp")
 _LIB_PATH = os.path.join(_HERE, "librtopk_oracle.so")
+# Host-sanitizer build (AddressSanitizer + UndefinedBehaviorSanitizer), used
+# instead of the plain one when ORACLE_SANITIZE=1. Python is not built with
+# ASan, so such a process needs the ASan runtime preloaded, e.g.
+#   LD_PRELOAD=$(g++ -print-file-name=libasan.so) ASAN_OPTIONS=detect_leaks=0 \
+#   ORACLE_SANITIZE=1 python -m pytest tests -m "not gpu"
+_SAN_LIB_PATH = os.path.join(_HERE, "librtopk_oracle_san.so")
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+              "-fno-omit-frame-pointer", "-g"]
 
 _lib = None
 
 
-def build() -> str:
-    """Compile the oracle with g++ (IEEE single precision, no contraction)."""
+def sanitized() -> bool:
+    """Whether this process loads the sanitizer build (ORACLE_SANITIZE=1)."""
+    return os.environ.get("ORACLE_SANITIZE", "") == "1"
+
+
+def build(sanitize: bool | None = None) -> str:
+    """Compile the oracle with g++ (IEEE single precision, no contraction).
+
+    sanitize (default: ORACLE_SANITIZE=1) builds the separate copy with
+    AddressSanitizer and UndefinedBehaviorSanitizer; the plain build is
+    left as it is.
+    """
+    if sanitize is None:
+        sanitize = sanitized()
+    out = _SAN_LIB_PATH if sanitize else _LIB_PATH
     cmd = [
         "g++", "-std=c++17", "-O2", "-fopenmp", "-ffp-contract=off",
-        "-fno-fast-math", "-fPIC", "-shared", "-o", _LIB_PATH + ".tmp", _SRC,
+        "-fno-fast-math", "-fPIC", "-shared", *(_SAN_FLAGS if sanitize else []),
+        "-o", out + ".tmp", _SRC,
     ]
     subprocess.run(cmd, check=True)
-    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
-    return _LIB_PATH
+    os.replace(out + ".tmp", out)
+    return out
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    path = _SAN_LIB_PATH if sanitized() else _LIB_PATH
+    if sanitized() or not os.path.exists(path):
         build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    lib = ctypes.CDLL(path)
     f32p = ctypes.POINTER(ctypes.c_float)
     i32p = ctypes.POINTER(ctypes.c_int32)
     lib.oracle_exact.argtypes = [f32p, ctypes.c_int64, ctypes.c_int32,
                                  ctypes.c_int32, f32p, i32p]
     lib.oracle_exact.restype = ctypes.c_int
+    lib.oracle_exact_by_sort.argtypes = [f32p, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_int32, f32p, i32p]
+    lib.oracle_exact_by_sort.restype = ctypes.c_int
     lib.oracle_capped.argtypes = [f32p, ctypes.c_int64, ctypes.c_int32,
                                   ctypes.c_int32, ctypes.c_int32,
                                   ctypes.c_float, ctypes.c_int32, f32p, i32p,
@@ -108,14 +136,28 @@ def _ip(a):
 
 
 def exact(x, k: int):
-    """Exact top-k of every row: (values [N,k] f32, indices [N,k] i32)."""
+    """Exact top-k of every row: (values [N,k] f32, indices [N,k] i32).
+
+    The k-th largest value of each row comes from a partial selection
+    (std::nth_element); survivors are the values above it, then the lowest
+    columns holding it."""
+    return _exact_with("oracle_exact", x, k)
+
+
+def exact_by_sort(x, k: int):
+    """The same result as ``exact`` through a full stable sort of each row
+    (a second, independent path for the tests)."""
+    return _exact_with("oracle_exact_by_sort", x, k)
+
+
+def _exact_with(fn: str, x, k: int):
     x = _as_rows(x)
     n, m = x.shape
     vals = np.empty((n, k), dtype=np.float32)
     idx = np.empty((n, k), dtype=np.int32)
-    rc = _load().oracle_exact(_fp(x), n, m, k, _fp(vals), _ip(idx))
+    rc = getattr(_load(), fn)(_fp(x), n, m, k, _fp(vals), _ip(idx))
     if rc != 0:
-        raise ValueError(f"oracle_exact: invalid arguments (N={n}, M={m}, k={k})")
+        raise ValueError(f"{fn}: invalid arguments (N={n}, M={m}, k={k})")
     return vals, idx
 
 

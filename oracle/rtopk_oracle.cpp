@@ -13,7 +13,10 @@
 //                     works": exactly k survivors per row). Where ties straddle
 //                     the k-th largest value, the lowest indices win. The
 //                     survivors are written in ascending index order (the pages
-//                     only ask for unsorted output).
+//                     only ask for unsorted output). The k-th largest value
+//                     comes from a partial selection (std::nth_element);
+//                     oracle_exact_by_sort reaches the same result through a
+//                     full stable sort, as a second path for the tests.
 //
 //   oracle_maxk_forward / oracle_maxk_backward -- the MaxK nonlinearity of
 //                     the MaxK-GNN review ("How MaxK-GNN works"): each row
@@ -60,7 +63,9 @@
 //                     (midpoint formula, count predicate, stop order, fill
 //                     order) is fixed in the comments of capped_row below.
 //
-// Build: g++ -std=c++17 -O2 -fopenmp -ffp-contract=off -fPIC -shared.
+// Build: g++ -std=c++17 -O2 -fopenmp -ffp-contract=off -fPIC -shared
+// (oracle/__init__.py; ORACLE_SANITIZE=1 builds a separate copy with
+// AddressSanitizer and UndefinedBehaviorSanitizer).
 // Floating point: IEEE single precision, round to nearest even, no FMA
 // contraction, subnormals kept (no fast-math, so the x87/SSE flush bits stay
 // clear). The only rounding the search performs is its midpoint.
@@ -94,10 +99,37 @@ void emit_ascending(const float* x, const std::vector<char>& chosen, int M,
   }
 }
 
-// Exact top-k of one row, straight from the definition: order the positions
-// by value, largest first, equal values by ascending position (a stable sort
-// of the positions under "greater value first"), and keep the first k.
+// Exact top-k of one row by partial selection: v_k, the k-th largest value,
+// is found with std::nth_element on a copy of the row; the survivors are
+// every position holding a value above v_k, then the lowest positions
+// holding v_k until there are k of them.
 void exact_row(const float* x, int M, int k, float* ov, int32_t* oi) {
+  std::vector<float> copy(x, x + M);
+  std::nth_element(copy.begin(), copy.begin() + (k - 1), copy.end(),
+                   [](float a, float b) { return a > b; });
+  const float vk = copy[k - 1];
+  std::vector<char> chosen(M, 0);
+  int taken = 0;
+  for (int j = 0; j < M; ++j) {
+    if (x[j] > vk) {
+      chosen[j] = 1;
+      ++taken;
+    }
+  }
+  for (int j = 0; j < M && taken < k; ++j) {
+    if (x[j] == vk) {
+      chosen[j] = 1;
+      ++taken;
+    }
+  }
+  emit_ascending(x, chosen, M, ov, oi);
+}
+
+// The same result by the textbook reduction, kept as an independent second
+// path for the tests: order the positions by value, largest first, equal
+// values by ascending position (a stable sort under "greater value first"),
+// and keep the first k.
+void exact_row_by_sort(const float* x, int M, int k, float* ov, int32_t* oi) {
   std::vector<int> order(M);
   std::iota(order.begin(), order.end(), 0);
   std::stable_sort(order.begin(), order.end(),
@@ -154,7 +186,7 @@ void capped_row(const float* x, int M, int k, int max_iter, float eps,
       hi = mid;
       break;
     }
-    if (c >= k)
+    if (c > k)
       lo = mid;
     else
       hi = mid;
@@ -194,6 +226,18 @@ int oracle_exact(const float* x, int64_t N, int32_t M, int32_t k,
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < N; ++r) {
     exact_row(x + r * M, M, k, out_val + r * k, out_idx + r * k);
+  }
+  return 0;
+}
+
+// Exact row-wise top-k through a stable sort of each row (exact_row_by_sort):
+// the same contract and result as oracle_exact, computed another way.
+int oracle_exact_by_sort(const float* x, int64_t N, int32_t M, int32_t k,
+                         float* out_val, int32_t* out_idx) {
+  if (N < 0 || M < 1 || k < 1 || k > M) return 1;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < N; ++r) {
+    exact_row_by_sort(x + r * M, M, k, out_val + r * k, out_idx + r * k);
   }
   return 0;
 }

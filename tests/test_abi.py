@@ -257,3 +257,36 @@ def test_sspmm_null_pointers(fn, which):
     ptrs[which] = None
     assert call(fn, ptrs[0], ptrs[1], ptrs[2], 4, 4, 4, ptrs[3], ptrs[4], 16, 4,
                 ptrs[5], None) == 1
+
+
+def _no_device() -> bool:
+    # Counting devices does not initialise the GPU on this image.
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+# Fully valid calls, each the first (or only) launch of its entry point. With
+# no device visible the launch itself fails: the call must report
+# RTOPK_ERROR_LAUNCH (and, for the two-kernel calls, stop before the second
+# launch). Never run where a GPU is visible: the pointers are not real.
+LAUNCH_CASES = [
+    ("rtopk_select", (FAKE, 4, 16, 4, 2, 0.0, FAKE, FAKE, None)),
+    ("rtopk_select_u8", (FAKE, 4, 16, 4, -1, 0.0, FAKE, FAKE, None)),
+    ("rtopk_select_exact", (FAKE, 4, 16, 4, FAKE, FAKE, None)),
+    ("rtopk_select_exact_u8", (FAKE, 4, 16, 4, FAKE, FAKE, None)),
+    ("rtopk_select_bucketed", (FAKE, 4, 16, 4, 2, FAKE, FAKE, None)),
+    ("rtopk_maxk_forward", (FAKE, 4, 16, 4, FAKE, FAKE, FAKE, None)),
+    ("rtopk_maxk_forward", (FAKE, 4, 2048, 4, FAKE, FAKE, FAKE, None)),  # two kernels
+    ("rtopk_maxk_backward", (FAKE, FAKE, 4, 16, 4, FAKE, None)),
+    ("rtopk_cbsr_spgemm", (FAKE, FAKE, FAKE, 4, 4, 600, FAKE, FAKE, 16, 4, FAKE, None)),
+    ("rtopk_cbsr_sspmm", (FAKE, FAKE, FAKE, 4, 4, 600, FAKE, FAKE, 16, 4, FAKE, None)),
+]
+
+
+@pytest.mark.skipif(not _no_device(), reason="needs a host with no GPU visible")
+@pytest.mark.parametrize("fn,args", LAUNCH_CASES, ids=[c[0] for c in LAUNCH_CASES])
+def test_launch_failure_maps_to_launch_status(fn, args):
+    assert call(fn, *args) == 3

@@ -7,7 +7,9 @@ indices; survivors are listed in ascending index order.
 
 Pins: exhaustive subset enumeration on every tiny row over a small alphabet
 (including -0 and +0), and invariants plus the sorted-value multiset on larger
-random and tie-heavy rows.
+random and tie-heavy rows. The oracle's partial-selection path
+(``oracle.exact``, std::nth_element) and its full stable-sort path
+(``oracle.exact_by_sort``) are both held to these pins and to each other.
 """
 
 import itertools
@@ -49,11 +51,12 @@ def test_exhaustive_small_rows(m):
     rows = np.array(list(itertools.product(range(len(alphabet)), repeat=m)))
     x = alphabet[rows].astype(np.float32)
     for k in range(1, m + 1):
-        vals, idx = oracle.exact(x, k)
         expect = brute_force_canonical(x, k)
-        assert (idx == expect).all(), f"m={m} k={k}"
         gathered = np.take_along_axis(x, expect, axis=1)
-        assert (vals.view(np.uint32) == gathered.view(np.uint32)).all()
+        for path in (oracle.exact, oracle.exact_by_sort):
+            vals, idx = path(x, k)
+            assert (idx == expect).all(), f"{path.__name__} m={m} k={k}"
+            assert (vals.view(np.uint32) == gathered.view(np.uint32)).all()
 
 
 @pytest.mark.parametrize("m,k", [(7, 3), (8, 8), (16, 5), (33, 1), (64, 17), (64, 64), (200, 32)])
@@ -65,6 +68,26 @@ def test_random_rows_invariants(m, k):
         vals, idx = oracle.exact(x, k)
         check_exact(x, vals, idx, k)
         assert canonical_ties_ok(x, vals, idx, k)
+
+
+@pytest.mark.parametrize("m", [1, 7, 64, 256, 1000, 4096])
+def test_partial_selection_equals_stable_sort(m):
+    # Two independent computations of the same definition must agree bit for
+    # bit (indices and value bits), ties and signed zeros included.
+    rng = np.random.default_rng(m)
+    families = [
+        rng.standard_normal((200, m)).astype(np.float32),
+        rng.integers(-2, 3, size=(200, m)).astype(np.float32),
+        np.round(4 * rng.standard_normal((200, m))).astype(np.float32) / 4,
+        np.where(rng.random((200, m)) < 0.5, np.float32(-0.0), np.float32(0.0)),
+        workloads.adversarial_rows(m),
+    ]
+    for x in families:
+        for k in sorted({1, max(1, m // 3), max(1, m - 1), m}):
+            a = oracle.exact(x, k)
+            b = oracle.exact_by_sort(x, k)
+            assert np.array_equal(a[1], b[1]), f"m={m} k={k}"
+            assert np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
 
 
 def test_adversarial_rows():
