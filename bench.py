@@ -36,6 +36,20 @@ KERNEL_SOURCES = ["rtopk_rows.hpp", "rtopk_dispatch.hip", "rtopk_internal.h",
                   "rtopk_maxk.hip", "rtopk_spgemm.hip", "rtopk_bucket.hip"]
 COPY_REF_BYTES = 2**28
 
+# The headline workload (bench.py with no flags).
+HEADLINE = {"rows": 262144, "m": 256, "k": 32, "mode": "exact", "max_iter": -1,
+            "eps": 0.0, "index": "u8", "inputs": "maxk"}
+# Named workloads (workloads.py): shape and first setting of each; sweeps
+# (k, eps, max_iter, row length) are chosen with the flags.
+CONFIGS = {
+    1: {"rows": 1024, "m": 256, "k": 32, "mode": "exact", "index": "i32"},
+    2: {"rows": 65536, "m": 256, "k": 32, "mode": "exact", "index": "i32"},
+    3: {"rows": 262144, "m": 256, "k": 32, "mode": "exact", "index": "u8"},
+    4: {"rows": 16384, "m": 8192, "k": 64, "mode": "exact", "index": "i32"},
+    5: {"rows": 1048576, "m": 1024, "k": 64, "mode": "capped", "max_iter": 2,
+        "index": "i32"},
+}
+
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
@@ -107,6 +121,10 @@ def record_traffic(workload: str, kernel: str, fetch_csv: str, write_csv: str) -
 
 
 def workload_name(args) -> str:
+    if args.config is not None and args.op == "select":
+        return (f"config {args.config} N={args.rows} M={args.m} k={args.k} {args.mode}"
+                + ("" if args.mode == "exact" else f" max_iter={args.max_iter} eps={args.eps}")
+                + f" idx={args.index}")
     if args.op in ("maxk_backward", "maxk_forward"):
         return f"{args.op} {args.inputs} N={args.rows} M={args.m} k={args.k} idx={args.index}"
     if args.op == "bucketed":
@@ -154,14 +172,18 @@ def parse():
                    help="mean degree of the power-law graph for --op spgemm")
     p.add_argument("--buckets", type=int, default=8,
                    help="buckets per row for --op bucketed")
-    p.add_argument("--rows", type=int, default=262144)
-    p.add_argument("--m", type=int, default=256)
-    p.add_argument("--k", type=int, default=32)
-    p.add_argument("--mode", choices=["exact", "capped"], default="exact")
-    p.add_argument("--max-iter", type=int, default=-1)
-    p.add_argument("--eps", type=float, default=0.0)
-    p.add_argument("--index", choices=["u8", "i32"], default="u8")
-    p.add_argument("--inputs", choices=["maxk", "normal", "grid"], default="maxk")
+    p.add_argument("--config", type=int, choices=sorted(CONFIGS), default=None,
+                   help="a named workload (workloads.py): its rows, row length, "
+                        "seed, k, mode and index width; flags given explicitly "
+                        "override them")
+    p.add_argument("--rows", type=int, default=None)
+    p.add_argument("--m", type=int, default=None)
+    p.add_argument("--k", type=int, default=None)
+    p.add_argument("--mode", choices=["exact", "capped"], default=None)
+    p.add_argument("--max-iter", type=int, default=None)
+    p.add_argument("--eps", type=float, default=None)
+    p.add_argument("--index", choices=["u8", "i32"], default=None)
+    p.add_argument("--inputs", choices=["maxk", "normal", "grid"], default=None)
     p.add_argument("--buffers", type=int, default=0,
                    help="input buffers to rotate (0: enough to exceed 768 MB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -172,7 +194,13 @@ def parse():
     p.add_argument("--copy-reference", action="store_true",
                    help="after timing, run a plain 256 MiB streaming kernel so that "
                         "a counter run can calibrate FETCH_SIZE / WRITE_SIZE")
-    return p.parse_args()
+    args = p.parse_args()
+    # Unset flags: the named workload's value, else the headline's.
+    named = CONFIGS.get(args.config, {})
+    for key, value in HEADLINE.items():
+        if getattr(args, key) is None:
+            setattr(args, key, named.get(key, value))
+    return args
 
 
 def main():
@@ -194,7 +222,9 @@ def main():
 
     n, m, k = args.rows, args.m, args.k
     u8 = args.index == "u8"
-    if args.inputs == "maxk":
+    if args.config is not None:
+        x_np = workloads.config_input(args.config, n, m)
+    elif args.inputs == "maxk":
         x_np = workloads.maxk_activation(n, m, workloads.CONFIG_SEEDS[3])
     elif args.inputs == "normal":
         x_np = workloads.normal(n, m, 6)
@@ -434,7 +464,10 @@ def main():
             elif args.mode == "exact":
                 oracle.exact(x_np[:r], k)
             else:
-                oracle.capped(x_np[:r], k, args.max_iter, args.eps)
+                # The per-row count numbers of the last pass are kept for the
+                # iteration report.
+                state["counts"] = oracle.capped(x_np[:r], k, args.max_iter, args.eps,
+                                                return_state=True)[2]
 
         def timed_passes(r, seconds):
             passes, spent = 0, 0.0
@@ -446,13 +479,28 @@ def main():
             return passes, spent
 
         # The oracle's SSpMM scatters into one accumulator on one thread.
+        state = {}
         cores = 1 if args.op == "sspmm" else oracle.threads()
         passes, t_cpu = timed_passes(n, args.cpu_seconds)
+        iterations = None
+        if "counts" in state:
+            # Counts the specified search made per row (RTop-K page,
+            # "Surprising findings": at eps = 0 it usually ends within 16).
+            cnt = state["counts"]
+            values, freq = np.unique(cnt, return_counts=True)
+            iterations = {"rows": int(cnt.size), "mean": float(cnt.mean()),
+                          "max": int(cnt.max()),
+                          "within_16": float((cnt <= 16).mean()),
+                          "histogram": {str(int(v)): int(f) for v, f in zip(values, freq)}}
         cpu = {"value": passes * n / t_cpu, "unit": "rows/s",
                "gbs": passes * n * per_row / t_cpu / 1e9,
                "cores": cores, "kind": "oracle",
+               "method": ("std::nth_element per row" if args.op == "select" and
+                          args.mode == "exact" else "the oracle of the op"),
                "sample": f"{passes} full pass(es) over the same {n}-row batch "
                          f"({t_cpu:.1f} s of oracle time)"}
+        if iterations is not None:
+            cpu["iterations"] = iterations
         # The same oracle on one thread, over the first rows of the batch (a
         # slice that one thread finishes in about two seconds).
         if cores == 1:

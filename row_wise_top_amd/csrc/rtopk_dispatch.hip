@@ -137,12 +137,17 @@ void exact_model(SelectArgs& a, int qc) {
 hipError_t launch_select(const SelectArgs& args, Mode mode, bool u8_index,
                          hipStream_t stream) {
   SelectArgs a = args;
-  // Candidate slots: the exact search compacts after its first count, the
-  // capped one once the bracket's lower end leaves at most 64*qc elements.
+  // The capped search with no cap and eps = 0 ends exactly where the exact
+  // search does (a count of k, or lo and hi adjacent floats with lo the k-th
+  // largest value; the tie fill then takes the lowest columns holding it),
+  // so the exact kernel computes it.
+  if (mode == Mode::kCapped && a.max_iter < 0 && a.eps == 0.0f) mode = Mode::kExact;
+  // Candidate slots: the exact search compacts after its first count; the
+  // capped search stages at the same model threshold (capped_row).
   const int q = slot_bucket(a.m);
   const int qc = mode == Mode::kCapped ? capped_candidate_slots(q, a.k, a.max_iter)
                                        : exact_candidate_slots(q, a.k);
-  if (mode != Mode::kCapped) exact_model(a, qc);
+  if (mode != Mode::kCapped || qc > 0) exact_model(a, qc);
   const RowsKernel fn = kernel_for(a.m, mode, u8_index, qc);
   if (fn == nullptr) return hipErrorInvalidValue;
   int device = 0;

@@ -109,27 +109,19 @@ inline int exact_candidate_slots(int q, int k) {
   return candidate_slots(q, k);
 }
 
-// Candidate slots of the capped search. Few steps (max_iter 1 to 3): the
-// widest window built for q slots (the largest of 8, 4, 2, 1 with
-// 2*QC <= q) that holds k, so that the search compacts as early as possible
-// (its thresholds are the specified midpoints, not aimed at the window).
-// More steps, or no cap: each step after the compaction costs QC compares,
-// so where the widest window is at least four times the exact search's,
-// the exact search's window. Measured at 1,048,576 x 1,024, k = 64 (QC 8
-// against 2, us): max_iter 2 897 / 1,022, 3 857 / 984, 4 855 / 840, 5 869 /
-// 838, 8 910 / 832, uncapped 935 / 839. At 262,144 x 256, k = 32 (QC 2
-// against 1) the wide window is as fast or faster at every max_iter.
+// Candidate slots of the capped search (see capped_row): the capped kernel
+// stages the elements above the exact search's first threshold (steered by
+// the exact search's model constants for this window) before its first
+// step, and every step then compares the candidate slots. Up to four steps:
+// the exact search's window (wider for long rows, so that more first counts
+// land in it); more steps, or no cap: the 2k window, whose steps compare
+// fewer slots (measured at 1,048,576 x 1,024, k = 64, 8 steps, with the
+// earlier compaction scheme: 832 us with 2 slots against 910 with 8). A
+// search with no cap and eps = 0 never reaches this: its result is the
+// canonical exact top-k, and launch_select runs the exact kernel for it.
 inline int capped_candidate_slots(int q, int k, int max_iter) {
-  int wide = 0;
-  for (int qc : {8, 4, 2, 1}) {
-    if (2 * qc <= q && kWave * qc >= k) {
-      wide = qc;
-      break;
-    }
-  }
-  const int narrow = candidate_slots(q, k);
-  if ((max_iter < 0 || max_iter >= 4) && narrow > 0 && wide >= 4 * narrow) return narrow;
-  return wide;
+  if (max_iter >= 0 && max_iter <= 4) return exact_candidate_slots(q, k);
+  return candidate_slots(q, k);
 }
 
 // Resident blocks per CU of `fn` launched with `threads` threads per block on

@@ -257,6 +257,21 @@ struct OutRow {
         spare(spare_word),
         col_base(first_col) {}
 
+  // Entry `pos` of the row: value bits and column (positions past the row's
+  // k entries are dropped by the buffer bounds). Used by StagedOut.
+  __device__ __forceinline__ void store_entry(uint32_t pos, uint32_t xbits,
+                                              uint32_t col) const {
+    __builtin_amdgcn_raw_buffer_store_b32(xbits, val, static_cast<int>(pos * 4u), 0,
+                                          kStoreNT);
+    if constexpr (sizeof(IdxT) == 1) {
+      __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(col), idx,
+                                           static_cast<int>(pos), 0, 0);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b32(col, idx, static_cast<int>(pos * 4u), 0,
+                                            kStoreNT);
+    }
+  }
+
   // Lanes whose bit of `msk` is set emit (x, col) as entry `rank` of the row;
   // the others store nothing.
   __device__ __forceinline__ void put(uint64_t msk, uint32_t rank, float x,
@@ -553,20 +568,236 @@ __device__ __forceinline__ void read_candidates(const uint32_t* __restrict__ scr
 // Capped search (rtopk_select): the specification in rtopk.h, step for step.
 // Invariant: #{x >= lo} >= k and (#{x >= hi} < k or hi == row max).
 //
-// Every threshold after a step that raised lo lies above lo, so once
-// #{x >= lo} fits the candidate window (64*QC), the remaining steps and the
-// tie fill only need the elements >= lo: they are compacted into QC slots
-// (as in the exact search) and the search carries on there, with QC
-// compares per count instead of Q and a fill over QC slots.
+// On this GPU the search is bound by instruction issue (vector and scalar
+// alike), so each step does only what the specification needs: the
+// midpoint, the split test, one count, two selects, and #{x >= hi} for the
+// tie fill. Where the count runs decides the cost; the host picks the
+// kernel's candidate slots QC by the number of steps:
+//  * QC == 0 (one or two steps): every count runs over the row and the tie
+//    fill too; narrowing would cost more than the few counts it saves.
+//  * QC > 0, stage first: one count at the exact search's first threshold t0 (aimed
+//    at the middle of the candidate window) also writes the elements >= t0
+//    to LDS. If that count c0 lands in (k, W], W = 64*QC, every specified
+//    step counts over those candidates only: for a midpoint >= t0 the count
+//    is the row's count, and for one below t0 it is c0 > k, which takes the
+//    same branch (lo rises) as the row's count would. The tie fill then runs
+//    over the candidates when lo >= t0 (every element >= lo is one of them),
+//    else over the row.
+//  * otherwise (the first count missed the window): steps over the row until
+//    #{x >= lo} fits the window, then the elements >= lo are compacted (every
+//    later threshold lies above lo, so counts over them are exact) and the
+//    search carries on there.
 // ---------------------------------------------------------------------------
+
+// Three wave-wide reductions interleaved (see wave_reduce2).
+template <class A, class B, class C>
+__device__ __forceinline__ void wave_reduce3(float& a, float& b, float& c) {
+  a = A::f(a, dpp<kQuadSwap1>(a));
+  b = B::f(b, dpp<kQuadSwap1>(b));
+  c = C::f(c, dpp<kQuadSwap1>(c));
+  a = A::f(a, dpp<kQuadSwap2>(a));
+  b = B::f(b, dpp<kQuadSwap2>(b));
+  c = C::f(c, dpp<kQuadSwap2>(c));
+  a = A::f(a, dpp<kRowHalfMirror>(a));
+  b = B::f(b, dpp<kRowHalfMirror>(b));
+  c = C::f(c, dpp<kRowHalfMirror>(c));
+  a = A::f(a, dpp<kRowMirror>(a));
+  b = B::f(b, dpp<kRowMirror>(b));
+  c = C::f(c, dpp<kRowMirror>(c));
+  a = A::f(a, dpp<kRowBcast15>(a));
+  b = B::f(b, dpp<kRowBcast15>(b));
+  c = C::f(c, dpp<kRowBcast15>(c));
+  a = A::f(a, dpp<kRowBcast31>(a));
+  b = B::f(b, dpp<kRowBcast31>(b));
+  c = C::f(c, dpp<kRowBcast31>(c));
+  a = lane63(a);
+  b = lane63(b);
+  c = lane63(c);
+}
+
+// Output rows assembled in LDS, for emissions over several slots: put()
+// writes a survivor's value bits and column at its rank in the wave's area
+// (value at entry e, column at entry KE + e, so one address serves both),
+// and flush() stores each array of the row with one coalesced store per 64
+// entries. Straight to memory, an emission over several slots writes each
+// 128-byte output line in parts, one store per slot. Lanes not selected
+// write the lane's spare entry k + lane; entries past k are never stored.
+// Ranks past k arise only when more than k elements tie at the row maximum:
+// with CLAMP (the area does not hold a whole row) they are clamped to the
+// spare entry.
+template <int KE, bool CLAMP>
+struct StagedOut {
+  uint32_t* area;
+  uint32_t spare;
+
+  __device__ __forceinline__ StagedOut(uint32_t* a, int k, int lane)
+      : area(a), spare(static_cast<uint32_t>(k + lane)) {}
+
+  __device__ __forceinline__ void put(uint64_t msk, uint32_t rank, float x,
+                                      int col) const {
+    uint32_t pos = lane_select(msk, rank, spare);
+    if constexpr (CLAMP) pos = min(pos, spare);
+    area[pos] = __float_as_uint(x);
+    area[KE + pos] = static_cast<uint32_t>(col);
+  }
+
+  // Store entries 0 .. k-1 through `out` (whose buffer bounds drop the
+  // positions past k of the last pass).
+  template <typename Out>
+  __device__ __forceinline__ void flush(const Out& out, int k, int lane) const {
+    // LDS operations of one wave complete in issue order; the barriers only
+    // keep the compiler from moving the reads across the writes.
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll 1
+    for (int base = 0; base < k; base += kWave) {
+      const uint32_t i = static_cast<uint32_t>(base + lane);
+      out.store_entry(i, area[i], area[KE + i]);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+};
+
+// The bracket (uniform values), #{x >= lo} (kept only while the search may
+// still compact), #{x >= hi} once a count has set hi (else -1), and the
+// number of counts made.
+struct CappedState {
+  float lo, hi;
+  int clo;
+  int chi;
+  uint32_t steps;
+};
+
+// One specified step on the elements in `w` (the row, or the candidates):
+// false once the search has stopped. A count of exactly k sets lo = hi = mid,
+// after which the split test (or the width test) ends the search at the next
+// step, exactly as the specified immediate stop would (nothing changes in
+// between). With eps = 0 the width test is implied by the split test and is
+// left out. TRACK: also keep #{x >= lo}.
+template <bool EPS0, bool TRACK, int S>
+__device__ __forceinline__ bool capped_step(const float (&w)[S], CappedState& b,
+                                            const SelectArgs& a) {
+  // max_iter < 0 (no cap) compares as the largest unsigned count.
+  if (!(b.steps < static_cast<uint32_t>(a.max_iter))) return false;
+  // Conditions on the uniform floats are taken as lane masks (all lanes
+  // agree), which the scalar unit tests directly.
+  if constexpr (!EPS0) {
+    if (ballot(b.hi - b.lo > a.eps) == 0) return false;
+  }
+  const float mid = 0.5f * b.lo + 0.5f * b.hi;
+  if ((ballot(b.lo < mid) & ballot(mid < b.hi)) == 0) return false;
+  const int c = count_ge(w, mid);
+  ++b.steps;
+  if constexpr (TRACK) b.clo = c >= a.k ? c : b.clo;
+  b.chi = c <= a.k ? c : b.chi;
+  b.lo = c >= a.k ? mid : b.lo;
+  b.hi = c <= a.k ? mid : b.hi;
+  return true;
+}
+
+// Steps until the search stops.
+template <bool EPS0, int S>
+__device__ __forceinline__ void capped_run(const float (&w)[S], CappedState& b,
+                                           const SelectArgs& a) {
+#pragma unroll 1
+  while (capped_step<EPS0, false>(w, b, a)) {
+  }
+}
+
+// Steps until the search stops (false) or #{x >= lo} fits `window` (true).
+template <bool EPS0, int S>
+__device__ __forceinline__ bool capped_run_until(const float (&w)[S],
+                                                 CappedState& b,
+                                                 const SelectArgs& a, int window) {
+#pragma unroll 1
+  for (;;) {
+    if (b.clo <= window) return true;
+    if (!capped_step<EPS0, true>(w, b, a)) return false;
+  }
+}
+
+// The tie fill over `w`, with #{x >= hi} taken from the search when a count
+// set hi (counted here only when hi is still the row maximum).
+// Whether a capped kernel has an LDS area to assemble output rows in: the
+// candidate staging area, or for rows of at most 512 columns without
+// candidates an area of a whole row (a few KB per wave).
+template <int Q, int QC>
+constexpr bool capped_staged_out() {
+  return QC > 0 || (Q > 1 && Q <= 8);
+}
+
+// Emissions over several slots go through `staged` (an LDS area holding the
+// row's k entries) where the kernel has one, else straight to `out`.
+template <bool STAGE, int S, typename Out, typename Staged, typename ColFn>
+__device__ __forceinline__ void capped_emit(const float (&w)[S], ColFn col,
+                                            const CappedState& b, int k,
+                                            const Out& out, const Staged& staged,
+                                            int lane) {
+  const int nA = b.chi >= 0 ? b.chi : count_ge(w, b.hi);
+  if constexpr (S == 1 || !STAGE) {
+    emit_fill(w, col, b.lo, b.hi, k, nA, out);
+  } else {
+    emit_fill(w, col, b.lo, b.hi, k, nA, staged);
+    staged.flush(out, k, lane);
+  }
+}
+
+// The tie fill when lo lies below the staging threshold t0 but hi does not
+// (hi is the row maximum or a midpoint whose count was at most k, both
+// >= t0): A = {x >= hi} lies wholly among the candidates, and only the
+// first k - nA elements of B = {lo <= x < hi} (by column) survive, which
+// usually sit in the row's first slot or two. So the row is scanned slot by
+// slot only until B's quota is met (the full second pass on those columns),
+// and the elements of A in later columns come from the candidates, which
+// are in column order. Writes exactly what emit_fill over the row would.
+template <int Q, int QC, typename Out>
+__device__ __forceinline__ void emit_fill_split(const float (&v)[Q],
+                                                const float (&cv)[QC],
+                                                const int (&ci)[QC], int lane,
+                                                float lo, float hi, int k, int nA,
+                                                const Out& out) {
+  if (nA >= k) {
+    // The first k of A, all candidates.
+    emit_fill(cv, [&ci](int s) { return ci[s]; }, lo, hi, k, nA, out);
+    return;
+  }
+  const uint32_t need = static_cast<uint32_t>(k - nA);
+  uint32_t base = 0, baseB = 0;
+  int end_col = kWave * Q;
+#pragma unroll
+  for (int s = 0; s < Q; ++s) {
+    if (baseB >= need) {
+      end_col = kWave * s;
+      break;
+    }
+    const uint64_t mA = ballot(v[s] >= hi);
+    const uint64_t mB = ballot(v[s] >= lo) & ~mA;
+    const uint64_t keepB = ballot(rank_below(mB, baseB) < need) & mB;
+    const uint64_t mS = mA | keepB;
+    out.put(mS, rank_below(mS, base), v[s], s * kWave + lane);
+    baseB += popc(mB);
+    base += popc(mS);
+  }
+#pragma unroll
+  for (int j = 0; j < QC; ++j) {
+    const uint64_t mA = ballot(cv[j] >= hi && ci[j] >= end_col);
+    out.put(mA, rank_below(mA, base), cv[j], ci[j]);
+    base += popc(mA);
+  }
+}
+
 template <int Q, bool FULL, int QC, typename Out>
 __device__ __forceinline__ void capped_row(const float (&vin)[Q],
                                            const SelectArgs& a, int lane,
                                            uint32_t* __restrict__ scratch,
                                            const Out& out) {
+  const int k = a.k;
   float v[Q];
+  float s2 = 0.0f;  // sum of squares (tail positions were read as 0)
 #pragma unroll
-  for (int s = 0; s < Q; ++s) v[s] = vin[s];
+  for (int s = 0; s < Q; ++s) {
+    v[s] = vin[s];
+    if constexpr (QC > 0) s2 = fmaf(vin[s], vin[s], s2);
+  }
   mask_tail<Q, FULL>(a.m, lane, v);
   float mn = kInf, mx = -kInf;
 #pragma unroll
@@ -575,65 +806,60 @@ __device__ __forceinline__ void capped_row(const float (&vin)[Q],
     mn = fminf(mn, FULL || v[s] > -kInf ? v[s] : kInf);
     mx = fmaxf(mx, v[s]);
   }
-  wave_reduce2<OpMin, OpMax>(mn, mx);
-  float lo = mn, hi = mx;
-  const int k = a.k;
-  int clo = a.m;  // #{x >= lo}
-  int chi = -1;   // #{x >= hi} once a count has set hi
-  int steps = 0;
-  // One specified step on the elements in `w` (the row, or the candidates):
-  // false once the search has stopped. Only the exit is a branch: a count of
-  // exactly k sets lo = hi = mid (and chi = k), after which the width test
-  // ends the search at the next step, exactly as the specified immediate
-  // stop would (nothing changes in between). With eps = 0 the width test is
-  // implied by lo < mid < hi and is left out.
-  auto step = [&](const auto& w, auto eps_zero) {
-    if (!(a.max_iter < 0 || steps < a.max_iter)) return false;
-    const float mid = 0.5f * lo + 0.5f * hi;
-    const bool wide = decltype(eps_zero)::value || hi - lo > a.eps;
-    if (!(wide && lo < mid && mid < hi)) return false;
-    const int c = count_ge(w, mid);
-    ++steps;
-    // Value selects, not branches: lo, hi and the counts stay uniform.
-    lo = c >= k ? mid : lo;
-    clo = c >= k ? c : clo;
-    hi = c <= k ? mid : hi;
-    chi = c <= k ? c : chi;
-    return true;
-  };
-  auto search = [&](auto eps_zero) {
-#pragma unroll 1
-    for (;;) {
-      if constexpr (QC > 0) {
-        if (clo <= kWave * QC) break;
-      }
-      if (!step(v, eps_zero)) return false;
-    }
-    return true;  // stopped with the candidates fitting the window
-  };
-  const bool compact = a.eps == 0.0f ? search(std::true_type{}) : search(std::false_type{});
-  if constexpr (QC > 0) {
-    if (compact) {
-      count_and_stage<Q, QC>(v, lo, lane, scratch);
-      float cv[QC];
-      int ci[QC];
-      read_candidates<Q, QC>(scratch, clo, lane, cv, ci);
-      auto rest = [&](auto eps_zero) {
-#pragma unroll 1
-        while (step(cv, eps_zero)) {
+  const bool eps0 = a.eps == 0.0f;
+  auto row_col = [lane](int s) { return s * kWave + lane; };
+  // The area the output rows are assembled in: the candidate staging area
+  // (free again once the candidates are in registers), which holds k + 64
+  // entries per array whenever a window is built, or for QC == 0 an area of
+  // a whole row (see rows_in_registers).
+  constexpr bool kStage = capped_staged_out<Q, QC>();
+  constexpr int kKE = QC > 0 ? stage_entries<Q, QC>() : kWave * Q + kWave;
+  const StagedOut<kKE, (!stage_whole_row<Q>() && QC > 0)> staged(scratch, k, lane);
+  if constexpr (QC == 0) {
+    wave_reduce2<OpMin, OpMax>(mn, mx);
+    CappedState b{mn, mx, a.m, -1, 0u};
+    if (eps0) capped_run<true>(v, b, a); else capped_run<false>(v, b, a);
+    capped_emit<kStage>(v, row_col, b, k, out, staged, lane);
+  } else {
+    constexpr int kW = kWave * QC;
+    float cv[QC];
+    int ci[QC];
+    auto cand_col = [&ci](int s) { return ci[s]; };
+    {
+      wave_reduce3<OpMin, OpMax, OpAdd>(mn, mx, s2);
+      CappedState b{mn, mx, a.m, -1, 0u};
+      // As in exact_row: r = sqrt(sum of squares), clamped so that the
+      // threshold stays finite; the model only chooses where to stage.
+      const float r = fminf(__builtin_amdgcn_sqrtf(s2), 1.0e35f);
+      const float t0 = r * a.z_first;
+      const int c0 = count_and_stage<Q, QC>(v, t0, lane, scratch);
+      if (c0 > k && c0 <= kW) {
+        read_candidates<Q, QC>(scratch, c0, lane, cv, ci);
+        if (eps0) capped_run<true>(cv, b, a); else capped_run<false>(cv, b, a);
+        // #{x >= hi} over the candidates is the row's: hi is the row maximum
+        // or a midpoint whose count was at most k, both >= t0.
+        if (ballot(b.lo >= t0) != 0) {
+          capped_emit<kStage>(cv, cand_col, b, k, out, staged, lane);
+        } else {
+          const int nA = b.chi >= 0 ? b.chi : count_ge(cv, b.hi);
+          emit_fill_split(v, cv, ci, lane, b.lo, b.hi, k, nA, staged);
+          staged.flush(out, k, lane);
         }
-      };
-      if (a.eps == 0.0f)
-        rest(std::true_type{});
-      else
-        rest(std::false_type{});
-      if (chi < 0) chi = count_ge(cv, hi);
-      emit_fill(cv, [&ci](int s) { return ci[s]; }, lo, hi, k, chi, out);
-      return;
+        return;
+      }
+      // The first count missed the window: the row from the start.
+      const bool fits = eps0 ? capped_run_until<true>(v, b, a, kW)
+                             : capped_run_until<false>(v, b, a, kW);
+      if (fits) {
+        count_and_stage<Q, QC>(v, b.lo, lane, scratch);
+        read_candidates<Q, QC>(scratch, b.clo, lane, cv, ci);
+        if (eps0) capped_run<true>(cv, b, a); else capped_run<false>(cv, b, a);
+        capped_emit<kStage>(cv, cand_col, b, k, out, staged, lane);
+      } else {
+        capped_emit<kStage>(v, row_col, b, k, out, staged, lane);
+      }
     }
   }
-  if (chi < 0) chi = count_ge(v, hi);
-  emit_fill(v, [lane](int s) { return s * kWave + lane; }, lo, hi, k, chi, out);
 }
 
 // Full-row search when the first count missed the candidate window: Newton
@@ -843,7 +1069,12 @@ template <int Q, bool FULL, Mode MODE, int QC, typename IdxT>
 __global__ __launch_bounds__(kWave * row_waves(Q)) void rows_in_registers(SelectArgs a) {
   // Per wave: the LDS staging area of the exact search, (value, column)
   // pairs (see stage_entries).
-  constexpr int kScratch = QC > 0 ? 2 * stage_entries<Q, QC>() : 1;
+  // Capped kernels without candidates: an area to assemble output rows in
+  // (see StagedOut), k + 64 <= 64*Q + 64 entries per array.
+  constexpr int kScratch =
+      QC > 0 ? 2 * stage_entries<Q, QC>()
+      : MODE == Mode::kCapped && capped_staged_out<Q, QC>() ? 2 * (kWave * Q + kWave)
+                                                             : 1;
   constexpr int D = prefetch_depth<Q, MODE>();
   constexpr int kRowWaves = row_waves(Q);
   // MaxK forward: the wave's LDS copy of the dense row (64*Q words) and one
@@ -870,6 +1101,11 @@ __global__ __launch_bounds__(kWave * row_waves(Q)) void rows_in_registers(Select
 #pragma unroll
     for (int d = 0; d < D; ++d)
       load_row<Q, FULL>(xg + min(d, rows - 1) * a.m, a.m, lane, buf[d]);
+    // Keep the group's loads here: without a memory barrier right after
+    // them, code generation sinks the loads of the later rows past the
+    // first row's search loop (the capped search), so that only one row is
+    // in flight while it waits. No wait is implied.
+    asm volatile("" ::: "memory");
     float* og = a.out_val + r * a.k;
     IdxT* ig = static_cast<IdxT*>(a.out_idx) + r * a.k;
     float* yg = kDense ? a.dense + r * a.m : nullptr;

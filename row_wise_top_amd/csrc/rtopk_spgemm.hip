@@ -326,9 +326,21 @@ __global__ __launch_bounds__(kBlock) void sspmm_rows(SpgemmArgs a) {
 
 }  // namespace spgemm_detail
 
+// Both two-kernel launches below size and check every launch before the
+// first one is enqueued, so that a configuration error enqueues nothing.
 hipError_t launch_sspmm(SpgemmArgs a, bool u8_index, hipStream_t stream) {
   using namespace spgemm_detail;
   const int64_t count = a.n_src * a.k;
+  a.chunk = kEdgesPerWave;
+  a.waves = a.nnz > 0 ? (a.nnz + a.chunk - 1) / a.chunk : 0;
+  a.m_pad = (a.m + 3) & ~3;
+  a.slots = a.k <= kWave ? (kWave / a.k < 4 ? kWave / a.k : 4) : 1;
+  const int per_wave_bytes =
+      (a.m_pad + 2 * static_cast<int>(kEdgesPerWave)) * static_cast<int>(sizeof(float));
+  int wpb = 65536 / per_wave_bytes;
+  a.waves_per_block = wpb < 1 ? 1 : (wpb > kWavesPerBlock ? kWavesPerBlock : wpb);
+  const int64_t blocks = (a.waves + a.waves_per_block - 1) / a.waves_per_block;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (count > 0) {
     int64_t zb = (count + kBlock - 1) / kBlock;
     zb = zb < 65536 ? zb : 65536;
@@ -338,16 +350,6 @@ hipError_t launch_sspmm(SpgemmArgs a, bool u8_index, hipStream_t stream) {
     if (err != hipSuccess) return err;
   }
   if (a.nnz == 0) return hipSuccess;
-  a.chunk = kEdgesPerWave;
-  a.waves = (a.nnz + a.chunk - 1) / a.chunk;
-  a.m_pad = (a.m + 3) & ~3;
-  a.slots = a.k <= kWave ? (kWave / a.k < 4 ? kWave / a.k : 4) : 1;
-  const int per_wave_bytes =
-      (a.m_pad + 2 * static_cast<int>(kEdgesPerWave)) * static_cast<int>(sizeof(float));
-  int wpb = 65536 / per_wave_bytes;
-  a.waves_per_block = wpb < 1 ? 1 : (wpb > kWavesPerBlock ? kWavesPerBlock : wpb);
-  const int64_t blocks = (a.waves + a.waves_per_block - 1) / a.waves_per_block;
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const size_t lds = static_cast<size_t>(a.waves_per_block) * per_wave_bytes;
   const dim3 block(kWave * a.waves_per_block);
   if (u8_index)

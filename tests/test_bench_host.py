@@ -103,3 +103,22 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_named_configs_and_overrides(monkeypatch):
+    import bench
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    a = bench.parse()
+    assert (a.rows, a.m, a.k, a.mode, a.index, a.inputs) == (262144, 256, 32, "exact", "u8", "maxk")
+    assert a.config is None and a.max_iter == -1 and a.eps == 0.0
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--config", "5"])
+    a = bench.parse()
+    assert (a.rows, a.m, a.k, a.mode, a.max_iter, a.index) == (1048576, 1024, 64, "capped", 2, "i32")
+    assert bench.workload_name(a).startswith("config 5 N=1048576 M=1024 k=64 capped max_iter=2")
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--config", "4", "--m", "2048", "--k", "128"])
+    a = bench.parse()
+    assert (a.rows, a.m, a.k, a.mode) == (16384, 2048, 128, "exact")
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--config", "2", "--mode", "capped",
+                                      "--max-iter", "4", "--eps", "1e-4"])
+    a = bench.parse()
+    assert (a.rows, a.k, a.max_iter, a.eps) == (65536, 32, 4, 1e-4)
