@@ -33,7 +33,8 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "rows/sec and achieved HBM GB/s (% of peak), N=262144 M=256 k=32 fp32"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["rtopk_rows.hpp", "rtopk_dispatch.hip", "rtopk_internal.h",
-                  "rtopk_maxk.hip", "rtopk_spgemm.hip", "rtopk_bucket.hip"]
+                  "rtopk_maxk.hip", "rtopk_spgemm.hip", "rtopk_bucket.hip",
+                  "rtopk_group.hpp"]
 COPY_REF_BYTES = 2**28
 
 # The headline workload (bench.py with no flags).

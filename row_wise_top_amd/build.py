@@ -32,7 +32,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["rtopk_api.hip", "rtopk_dispatch.hip", "rtopk_rows_a.hip",
            "rtopk_rows_b.hip", "rtopk_rows_c.hip", "rtopk_rows_d.hip",
            "rtopk_rows_e.hip", "rtopk_rows_f.hip", "rtopk_maxk.hip",
-           "rtopk_spgemm.hip", "rtopk_bucket.hip"]
+           "rtopk_spgemm.hip", "rtopk_bucket.hip", "rtopk_group.hip"]
 ARCH = "gfx950"
 
 # The one line the host pass prints for the device-only feature (see above).

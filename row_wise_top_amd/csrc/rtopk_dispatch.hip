@@ -132,6 +132,29 @@ void exact_model(SelectArgs& a, int qc) {
   last = Model{a.m, a.k, qc, a.z_first, a.half_step, a.z_first_c, a.half_step_c, a.inv_m};
 }
 
+// Exact search on rows longer than kGroupMinLength: one row per block of
+// four waves (rtopk_group.hpp), on a persistent grid of what fits on the
+// device at once.
+hipError_t launch_group(const SelectArgs& a, int qc, hipStream_t stream) {
+  constexpr int kPerSlot = kWave * kWavesPerRowGroup;
+  const int per_wave = (a.m + kPerSlot - 1) / kPerSlot;
+  const int q = per_wave <= 24 ? 24 : 32;
+  const bool full = a.m == q * kPerSlot;
+  const RowsKernel fn = q == 24 ? group_kernel<24>(full, false, qc)
+                                : group_kernel<32>(full, false, qc);
+  if (fn == nullptr) return hipErrorInvalidValue;
+  int device = 0;
+  hipError_t err = hipGetDevice(&device);
+  if (err != hipSuccess) return err;
+  const int threads = kWave * kWavesPerRowGroup;
+  const int64_t resident =
+      static_cast<int64_t>(cu_count(device)) *
+      resident_blocks(reinterpret_cast<const void*>(fn), threads, device);
+  const int64_t grid = a.n < resident ? a.n : resident;
+  hipLaunchKernelGGL(fn, dim3(static_cast<uint32_t>(grid)), dim3(threads), 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_select(const SelectArgs& args, Mode mode, bool u8_index,
@@ -148,6 +171,8 @@ hipError_t launch_select(const SelectArgs& args, Mode mode, bool u8_index,
   const int qc = mode == Mode::kCapped ? capped_candidate_slots(q, a.k, a.max_iter)
                                        : exact_candidate_slots(q, a.k);
   if (mode != Mode::kCapped || qc > 0) exact_model(a, qc);
+  if (mode == Mode::kExact && a.m > kGroupMinLength && !u8_index)
+    return launch_group(a, qc, stream);
   const RowsKernel fn = kernel_for(a.m, mode, u8_index, qc);
   if (fn == nullptr) return hipErrorInvalidValue;
   int device = 0;

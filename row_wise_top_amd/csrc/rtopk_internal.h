@@ -20,6 +20,11 @@ constexpr int kBlock = kWave * kWavesPerBlock;
 // does), four waves for longer rows.
 constexpr int row_waves(int q) { return q <= 8 ? 1 : 4; }
 
+// Waves that share one row in the row-group kernel (rtopk_group.hpp), used
+// by the exact search for rows longer than kGroupMinLength.
+constexpr int kWavesPerRowGroup = 4;
+constexpr int kGroupMinLength = 4096;
+
 // kMaxk: the exact search, plus the dense [n, m] MaxK output (SelectArgs::dense).
 // kBucket: the exact search on buckets: each kernel row is one bucket of an
 // input row (SelectArgs::buckets of them, m columns each) and emitted
@@ -79,6 +84,11 @@ constexpr int kSlotBuckets[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 12
 // qc: candidate slots of the exact search (0: no compaction).
 template <int Q>
 RowsKernel rows_kernel(bool full, Mode mode, bool u8_index, int qc);
+
+// Defined in rtopk_group.hpp, instantiated in rtopk_group.hip: the exact
+// kernel for rows held by a group of four waves, q slots per lane per wave.
+template <int Q>
+RowsKernel group_kernel(bool full, bool u8_index, int qc);
 
 // Candidate slots QC the exact search compacts into for q slots and k
 // survivors: the smallest of 1, 2, 4, 8 with 64*QC >= 2k and 2*QC <= q, or 0

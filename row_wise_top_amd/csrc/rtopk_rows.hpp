@@ -673,7 +673,7 @@ struct CappedState {
 // step, exactly as the specified immediate stop would (nothing changes in
 // between). With eps = 0 the width test is implied by the split test and is
 // left out. TRACK: also keep #{x >= lo}.
-template <bool EPS0, bool TRACK, int S>
+template <bool EPS0, bool TRACK, int S, bool CHI = true>
 __device__ __forceinline__ bool capped_step(const float (&w)[S], CappedState& b,
                                             const SelectArgs& a) {
   // max_iter < 0 (no cap) compares as the largest unsigned count.
@@ -688,19 +688,23 @@ __device__ __forceinline__ bool capped_step(const float (&w)[S], CappedState& b,
   const int c = count_ge(w, mid);
   ++b.steps;
   if constexpr (TRACK) b.clo = c >= a.k ? c : b.clo;
-  b.chi = c <= a.k ? c : b.chi;
+  if constexpr (CHI) b.chi = c <= a.k ? c : b.chi;
   b.lo = c >= a.k ? mid : b.lo;
   b.hi = c <= a.k ? mid : b.hi;
   return true;
 }
 
-// Steps until the search stops.
+// Steps until the search stops. Over the candidates (S <= 2 slots) the
+// steps leave #{x >= hi} to a count at the end, which costs less than
+// keeping it at every step.
 template <bool EPS0, int S>
 __device__ __forceinline__ void capped_run(const float (&w)[S], CappedState& b,
                                            const SelectArgs& a) {
+  constexpr bool kChi = S > 2;
 #pragma unroll 1
-  while (capped_step<EPS0, false>(w, b, a)) {
+  while (capped_step<EPS0, false, S, kChi>(w, b, a)) {
   }
+  if constexpr (!kChi) b.chi = -1;
 }
 
 // Steps until the search stops (false) or #{x >= lo} fits `window` (true).
