@@ -31,7 +31,14 @@ rtopk_status_t run(const float* x, int64_t n, int32_t m, int32_t k,
   if (st != RTOPK_SUCCESS) return st;
   if (n == 0) return RTOPK_SUCCESS;
   rtopk::SelectArgs a{x, n, m, k, max_iter, eps, out_val, out_idx, 0.0f, 0.0f, nullptr, 1};
-  const hipError_t err = rtopk::launch_select(a, mode, u8_index, stream);
+  // Short rows keeping few survivors, exact: one lane per row, 64 rows per
+  // wave (the bucket kernel with one bucket per row), instead of one row per
+  // wave with most lanes idle.
+  const bool exact = mode == rtopk::Mode::kExact ||
+                     (mode == rtopk::Mode::kCapped && max_iter < 0 && eps == 0.0f);
+  const hipError_t err = exact && rtopk::bucket_lanes_supported(m, k)
+                             ? rtopk::launch_bucket_lanes(a, u8_index, stream)
+                             : rtopk::launch_select(a, mode, u8_index, stream);
   return err == hipSuccess ? RTOPK_SUCCESS : RTOPK_ERROR_LAUNCH;
 }
 

@@ -174,11 +174,14 @@ __global__ __launch_bounds__((lane_waves<W, VEC>() * kWave)) void bucket_lanes(S
   if constexpr (KB <= 2) {
     // The KB best so far with their columns, largest first. Empty places
     // hold -inf (inputs are finite, so the first KB elements always enter).
-    float tv[KB];
+    // The survivors are carried as bits (integer selects): a float select
+    // `x > t ? x : t` may be folded into a maximum, which need not keep the
+    // sign of a zero that ties.
+    uint32_t tb[KB];
     int tc[KB];
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
-      tv[i] = -__builtin_inff();
+      tb[i] = __float_as_uint(-__builtin_inff());
       tc[i] = i;
     }
 #pragma unroll
@@ -186,31 +189,32 @@ __global__ __launch_bounds__((lane_waves<W, VEC>() * kWave)) void bucket_lanes(S
       // Straight-line code over all W places (no loop the compiler could
       // roll up and index registers in).
       const float x = v[j];
+      const uint32_t xb = __float_as_uint(x);
       bool gt[KB];
 #pragma unroll
-      for (int i = 0; i < KB; ++i) gt[i] = x > tv[i];
+      for (int i = 0; i < KB; ++i) gt[i] = x > __uint_as_float(tb[i]);
       // Insert x above every element it beats: place i takes the element of
       // place i - 1 if x beats that one too, else x if x beats place i.
 #pragma unroll
       for (int i = KB - 1; i > 0; --i) {
-        tv[i] = gt[i - 1] ? tv[i - 1] : (gt[i] ? x : tv[i]);
+        tb[i] = gt[i - 1] ? tb[i - 1] : (gt[i] ? xb : tb[i]);
         tc[i] = gt[i - 1] ? tc[i - 1] : (gt[i] ? j : tc[i]);
       }
-      tv[0] = gt[0] ? x : tv[0];
+      tb[0] = gt[0] ? xb : tb[0];
       tc[0] = gt[0] ? j : tc[0];
     }
     if constexpr (KB == 2) {
       // Column order (with kb == 1 the second place is dropped anyway).
       const bool sw = kb == 2 && tc[0] > tc[1];
-      const float v0 = tv[0];
+      const uint32_t b0 = tb[0];
       const int c0 = tc[0];
-      tv[0] = sw ? tv[1] : tv[0];
+      tb[0] = sw ? tb[1] : tb[0];
       tc[0] = sw ? tc[1] : tc[0];
-      tv[1] = sw ? v0 : tv[1];
+      tb[1] = sw ? b0 : tb[1];
       tc[1] = sw ? c0 : tc[1];
     }
 #pragma unroll
-    for (int i = 0; i < KB; ++i) put(i, tv[i], static_cast<uint32_t>(tc[i]));
+    for (int i = 0; i < KB; ++i) put(i, __uint_as_float(tb[i]), static_cast<uint32_t>(tc[i]));
   } else {
     // The KB largest values (a multiset, largest first) by median-of-three
     // insertion: with tv sorted, place i becomes med3(tv[i-1], x, tv[i]).

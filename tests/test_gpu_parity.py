@@ -298,3 +298,33 @@ def test_nonnull_stream():
         v, i = r.rtopk_select_exact(x, 32)
     s.synchronize()
     assert_identical((v.cpu().numpy(), i.cpu().numpy()), oracle.exact(x_np, 32), "stream")
+
+
+# Short rows with few survivors take one lane per row (64 rows per wave):
+# row lengths around the 8/16/32/64-column classes, every survivor class,
+# row counts that end inside a wave, tie-heavy and adversarial rows, and an
+# input that starts one float past a 16-byte boundary (4-byte loads).
+@pytest.mark.parametrize("m", [1, 3, 8, 9, 16, 17, 31, 32, 33, 63, 64])
+def test_short_rows_many_per_wave(m):
+    rng = np.random.default_rng(500 + m)
+    for n in (1, 63, 64, 65, 1000, 4097):
+        for k in sorted({1, 2, 3, 5, 8} & set(range(1, m + 1))):
+            fam = (n + k) % 3
+            if fam == 0:
+                x = rng.standard_normal((n, m)).astype(np.float32)
+            elif fam == 1:
+                x = rng.integers(-2, 3, size=(n, m)).astype(np.float32)
+            else:
+                x = np.tile(workloads.adversarial_rows(m), (n // 16 + 1, 1))[:n]
+            x = np.ascontiguousarray(x) + np.float32(0.0)
+            check(x, k, "exact", label=f"short M={m} n={n}")
+            check(x, k, "exact", u8=True, label=f"short M={m} n={n}")
+            if n == 1000:
+                check(x, k, "capped", -1, 0.0, label=f"short uncapped M={m}")
+    # Misaligned start: a view one float into a padded buffer.
+    x = workloads.normal(777, m, seed=m)
+    buf = torch.zeros(777 * m + 1, dtype=torch.float32, device=dev())
+    buf[1:].copy_(torch.from_numpy(x.reshape(-1)))
+    xt = buf[1:].view(777, m)
+    for k in sorted({1, 4, 8} & set(range(1, m + 1))):
+        assert_identical(gpu_run_t(xt, k, "exact"), oracle.exact(x, k), f"short misaligned M={m}")
