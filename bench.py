@@ -32,9 +32,19 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "rows/sec and achieved HBM GB/s (% of peak), N=262144 M=256 k=32 fp32"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["rtopk_rows.hpp", "rtopk_dispatch.hip", "rtopk_internal.h",
-                  "rtopk_maxk.hip", "rtopk_spgemm.hip", "rtopk_bucket.hip",
-                  "rtopk_group.hpp"]
+# Sources each kernel family is built from, beside the dispatch code every
+# launch goes through: a counter record stays valid while these are unchanged
+# (a change to the aggregation kernels leaves the selection's records valid).
+_DISPATCH_SOURCES = ["rtopk_api.hip", "rtopk_internal.h", "rtopk_dispatch.hip"]
+FAMILY_SOURCES = {
+    "rows_in_registers": ["rtopk_rows.hpp"],
+    "rows_in_group": ["rtopk_rows.hpp", "rtopk_group.hpp"],
+    "bucket_lanes": ["rtopk_bucket.hip"],
+    "scatter_rows": ["rtopk_maxk.hip"],
+    "spgemm_rows": ["rtopk_spgemm.hip"],
+    "sspmm_rows": ["rtopk_spgemm.hip"],
+}
+KERNEL_SOURCES = sorted({f for v in FAMILY_SOURCES.values() for f in v} | set(_DISPATCH_SOURCES))
 COPY_REF_BYTES = 2**28
 
 # The headline workload (bench.py with no flags).
@@ -52,24 +62,36 @@ CONFIGS = {
 }
 
 
-def kernel_source_hash() -> str:
+def kernel_family(kernel: str) -> str:
+    """Family of a kernel name fragment from op_kernel(): the register-resident
+    row kernels are told apart by their mode argument."""
+    return "rows_in_registers" if kernel.startswith("(rtopk::Mode)") else kernel
+
+
+def kernel_source_hash(kernel: str | None = None) -> str:
+    """Hash of the sources of the kernel named by an op_kernel() fragment and
+    of the dispatch code (all kernel sources if None)."""
+    if kernel is None:
+        names = KERNEL_SOURCES
+    else:
+        names = sorted(set(FAMILY_SOURCES[kernel_family(kernel)]) | set(_DISPATCH_SOURCES))
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "row_wise_top_amd", "csrc")
-    for name in KERNEL_SOURCES:
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources for this workload."""
+    were taken on the current sources of the kernel for this workload."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_hash") != kernel_source_hash():
+    if not rec or rec.get("kernel_hash") != kernel_source_hash(kernel):
         return None
     return float(rec["bytes_per_launch"])
 
@@ -110,7 +132,7 @@ def record_traffic(workload: str, kernel: str, fetch_csv: str, write_csv: str) -
             data = json.load(f)
     except (OSError, ValueError):
         data = {}
-    data[workload] = {"kernel_hash": kernel_source_hash(),
+    data[workload] = {"kernel_hash": kernel_source_hash(kernel), "kernel": kernel,
                       "bytes_per_launch": fetched + written,
                       "fetch_bytes": fetched, "write_bytes": written,
                       "fetch_kib_raw": f_sel, "write_kib_raw": w_sel,
@@ -140,9 +162,10 @@ def workload_name(args) -> str:
 
 
 def op_kernel(args) -> str:
-    """Name fragment of the kernel the op launches, for the counter records
-    (specific enough to leave out the exact selection the approximate ops
-    run once for their quality figures)."""
+    """Name fragment of the kernel the op's counters are attributed to, as the
+    library routes the workload (specific enough to leave out the exact
+    selection the approximate ops run once for their quality figures)."""
+    index = getattr(args, "index", "i32")
     if args.op == "maxk_backward":
         return "scatter_rows"
     if args.op in ("spgemm", "sspmm"):
@@ -151,8 +174,19 @@ def op_kernel(args) -> str:
         width, kb = args.m // args.buckets, args.k // args.buckets
         return "bucket_lanes" if width <= 64 and kb <= 8 else "(rtopk::Mode)3"
     if args.op == "maxk_forward":
-        return "(rtopk::Mode)2"
-    return "(rtopk::Mode)1" if args.mode == "exact" else "(rtopk::Mode)0"
+        if args.m <= 1024:
+            return "(rtopk::Mode)2"
+        return "rows_in_group" if args.m > 4096 else "(rtopk::Mode)1"
+    # Selection: no cap and eps = 0 is the exact selection.
+    exact = args.mode == "exact" or (getattr(args, "max_iter", 0) < 0
+                                     and getattr(args, "eps", 1.0) == 0.0)
+    if not exact:
+        return "(rtopk::Mode)0"
+    if args.m <= 64 and args.k <= 8:
+        return "bucket_lanes"
+    if args.m > 4096 and index != "u8":
+        return "rows_in_group"
+    return "(rtopk::Mode)1"
 
 
 def parse():
@@ -424,7 +458,7 @@ def main():
     algo_bytes = int(n * per_row)
     achieved = algo_bytes / (avg_launch_ms * 1e-3) / 1e9
     workload = workload_name(args)
-    traffic = measured_traffic(workload)
+    traffic = measured_traffic(workload, op_kernel(args))
 
     # Approximate ops: hit rate and relative errors against the library's exact
     # selection of the same rows (definitions in row_wise_top_amd/quality.py).

@@ -50,12 +50,13 @@ def test_record_traffic_calibrates_both_counters(tmp_path, monkeypatch):
     assert rec["fetch_bytes"] == pytest.approx(1001.0 * 1024 * 2)
     assert rec["write_bytes"] == pytest.approx(160.0 * 1024)
     assert rec["bytes_per_launch"] == pytest.approx(1001.0 * 2048 + 160.0 * 1024)
-    assert rec["kernel_hash"] == bench.kernel_source_hash()
+    assert rec["kernel_hash"] == bench.kernel_source_hash("(rtopk::Mode)1")
     # The stored figure is served back only while the sources are unchanged.
-    assert bench.measured_traffic("wl") == pytest.approx(rec["bytes_per_launch"])
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "changed")
-    assert bench.measured_traffic("wl") is None
-    assert bench.measured_traffic("other workload") is None
+    assert bench.measured_traffic("wl", "(rtopk::Mode)1") == pytest.approx(rec["bytes_per_launch"])
+    assert bench.measured_traffic("wl", "bucket_lanes") is None
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda kernel=None: "changed")
+    assert bench.measured_traffic("wl", "(rtopk::Mode)1") is None
+    assert bench.measured_traffic("other workload", "(rtopk::Mode)1") is None
 
 
 def test_counters_of_other_kernels_are_left_out(tmp_path, monkeypatch):
@@ -81,21 +82,36 @@ def test_missing_records_are_an_error(tmp_path):
         bench._counter_means(str(tmp_path / "f.csv"), "FETCH_SIZE", "(rtopk::Mode)1")
 
 
-@pytest.mark.parametrize("op,mode,m,k,buckets,want", [
-    ("select", "exact", 256, 32, 1, "(rtopk::Mode)1"),
-    ("select", "capped", 256, 32, 1, "(rtopk::Mode)0"),
-    ("maxk_forward", "exact", 256, 32, 1, "(rtopk::Mode)2"),
-    ("maxk_backward", "exact", 256, 32, 1, "scatter_rows"),
-    ("bucketed", "exact", 256, 32, 8, "bucket_lanes"),
-    ("bucketed", "exact", 256, 32, 4, "bucket_lanes"),
-    ("bucketed", "exact", 256, 32, 2, "(rtopk::Mode)3"),
-    ("bucketed", "exact", 256, 64, 2, "(rtopk::Mode)3"),
-    ("spgemm", "exact", 256, 32, 1, "spgemm_rows"),
-    ("sspmm", "exact", 256, 32, 1, "sspmm_rows"),
+@pytest.mark.parametrize("op,mode,m,k,buckets,index,want", [
+    ("select", "exact", 256, 32, 1, "u8", "(rtopk::Mode)1"),
+    ("select", "capped", 256, 32, 1, "u8", "(rtopk::Mode)0"),
+    ("select", "exact", 64, 8, 1, "u8", "bucket_lanes"),
+    ("select", "exact", 128, 16, 1, "u8", "(rtopk::Mode)1"),
+    ("select", "exact", 8192, 64, 1, "i32", "rows_in_group"),
+    ("select", "exact", 4096, 64, 1, "i32", "(rtopk::Mode)1"),
+    ("maxk_forward", "exact", 256, 32, 1, "u8", "(rtopk::Mode)2"),
+    ("maxk_forward", "exact", 8192, 32, 1, "i32", "rows_in_group"),
+    ("maxk_backward", "exact", 256, 32, 1, "u8", "scatter_rows"),
+    ("bucketed", "exact", 256, 32, 8, "u8", "bucket_lanes"),
+    ("bucketed", "exact", 256, 32, 4, "u8", "bucket_lanes"),
+    ("bucketed", "exact", 256, 32, 2, "u8", "(rtopk::Mode)3"),
+    ("bucketed", "exact", 256, 64, 2, "u8", "(rtopk::Mode)3"),
+    ("spgemm", "exact", 256, 32, 1, "u8", "spgemm_rows"),
+    ("sspmm", "exact", 256, 32, 1, "u8", "sspmm_rows"),
 ])
-def test_op_kernel(op, mode, m, k, buckets, want):
-    args = argparse.Namespace(op=op, mode=mode, m=m, k=k, buckets=buckets)
+def test_op_kernel(op, mode, m, k, buckets, index, want):
+    args = argparse.Namespace(op=op, mode=mode, m=m, k=k, buckets=buckets, index=index,
+                              max_iter=4, eps=0.0)
     assert bench.op_kernel(args) == want
+
+
+def test_uncapped_search_is_counted_as_the_exact_kernel():
+    # No cap and eps = 0 runs the exact selection.
+    args = argparse.Namespace(op="select", mode="capped", m=256, k=32, buckets=1,
+                              index="u8", max_iter=-1, eps=0.0)
+    assert bench.op_kernel(args) == "(rtopk::Mode)1"
+    args.eps = 1e-4
+    assert bench.op_kernel(args) == "(rtopk::Mode)0"
 
 
 def test_more_than_one_gpu_is_refused():
@@ -122,3 +138,16 @@ def test_named_configs_and_overrides(monkeypatch):
                                       "--max-iter", "4", "--eps", "1e-4"])
     a = bench.parse()
     assert (a.rows, a.k, a.max_iter, a.eps) == (65536, 32, 4, 1e-4)
+
+
+def test_source_hash_is_per_kernel():
+    # A change to the aggregation kernels leaves the selection's records valid.
+    assert set(bench.FAMILY_SOURCES["spgemm_rows"]).isdisjoint(
+        bench.FAMILY_SOURCES["rows_in_registers"])
+    assert bench.kernel_source_hash("(rtopk::Mode)1") != bench.kernel_source_hash("spgemm_rows")
+    assert bench.kernel_source_hash("(rtopk::Mode)1") == bench.kernel_source_hash("(rtopk::Mode)0")
+    assert bench.kernel_source_hash("(rtopk::Mode)1") != bench.kernel_source_hash("bucket_lanes")
+    for fam in bench.FAMILY_SOURCES:
+        assert len(bench.kernel_source_hash(fam)) == 16
+        for name in bench.FAMILY_SOURCES[fam]:
+            assert os.path.exists(os.path.join(ROOT, "row_wise_top_amd", "csrc", name))
