@@ -73,84 +73,18 @@ template <int W, bool VEC>
 constexpr bool lane_stage() {
   return VEC && W >= 32;
 }
-// Waves per block: one, so that a block's LDS (17 KB for the 64-column
-// stage) frees as soon as its wave ends (measured 1-2% faster than four
-// waves for 8 and 32 buckets of 256 columns, 7% for 4 buckets).
-template <int W, bool VEC>
-constexpr int lane_waves() {
-  return 1;
-}
 
-template <int W, int KB, bool VEC, typename IdxT>
-__global__ __launch_bounds__((lane_waves<W, VEC>() * kWave)) void bucket_lanes(SelectArgs a) {
-  constexpr bool kStage = lane_stage<W, VEC>();
-  constexpr int kWaves = lane_waves<W, VEC>();
-  // LDS row of a lane: W + 4 floats (16-byte aligned; the skew of 4 banks
-  // per row keeps 8 consecutive lanes on distinct banks for both the writes
-  // and the reads below).
-  constexpr int kStride = W + 4;
-  __shared__ u32x4 stage_all[kStage ? kWaves : 1][kStage ? kWave * kStride / 4 : 1];
-  const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
-  const int wave_in_block =
-      __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-  const int64_t g0 =
-      static_cast<int64_t>(blockIdx.x) * (kWaves * kWave) + wave_in_block * kWave;
-  if (g0 >= a.n) return;
+// One lane's bucket of a group of 64 consecutive buckets starting at bucket
+// g0 (live of them exist): v holds its W places (-inf past w), `row` is its
+// LDS row when the group was staged (values of survivors are read back from
+// there), else the bucket is read again from memory through rx at byte
+// offset `base`. Finds the bucket's kb best and writes them lowest column
+// first to entries [g*kb, g*kb + kb) of the outputs.
+template <int W, int KB, bool kStage, typename IdxT>
+__device__ __forceinline__ void select_bucket(const SelectArgs& a, int64_t g0, int live, int lane,
+                                              const float (&v)[W], const float* row,
+                                              __amdgpu_buffer_rsrc_t rx, int base) {
   const int w = a.m, kb = a.k;
-  const int live = a.n - g0 < kWave ? static_cast<int>(a.n - g0) : kWave;
-  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(a.x + g0 * w), 0, live * w * 4, kRsrcWord3);
-  // Elements past the bucket (j >= w) belong to the next one and are never
-  // considered.
-  const int base = lane * w * 4;
-  float v[W];
-  u32x4* stage = stage_all[kStage ? wave_in_block : 0];
-  if constexpr (kStage) {
-    // Chunk c = 64 i + lane (16 bytes) is place 4 (c mod (W/4)) of bucket
-    // c / (W/4). Chunks past the bucket (w is a multiple of 4) or past the
-    // buckets the wave has are not written; those places are never read as
-    // part of a bucket.
-    constexpr int kChunks = W / 4;  // chunks per bucket
-#pragma unroll
-    for (int i = 0; i < W / 4; ++i) {
-      const int c = i * kWave + lane;
-      const int bkt = c / kChunks;
-      const int p = 4 * (c % kChunks);
-      const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(rx, (bkt * w + p) * 4, 0, kLoadPolicy);
-      if (p < w && bkt < live) stage[(bkt * kStride + p) / 4] = q;
-    }
-    // LDS operations of one wave complete in issue order; the barrier keeps
-    // the compiler from moving the reads above the writes.
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int j = 0; j < W; j += 4) {
-      const u32x4 q = stage[(lane * kStride + j) / 4];
-      v[j] = __uint_as_float(q.x);
-      v[j + 1] = __uint_as_float(q.y);
-      v[j + 2] = __uint_as_float(q.z);
-      v[j + 3] = __uint_as_float(q.w);
-    }
-  } else if constexpr (VEC) {
-#pragma unroll
-    for (int j = 0; j < W; j += 4) {
-      const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(rx, base + j * 4, 0, kLoadPolicy);
-      v[j] = __uint_as_float(q.x);
-      v[j + 1] = __uint_as_float(q.y);
-      v[j + 2] = __uint_as_float(q.z);
-      v[j + 3] = __uint_as_float(q.w);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < W; ++j)
-      v[j] = __uint_as_float(
-          __builtin_amdgcn_raw_buffer_load_b32(rx, base + j * 4, 0, kLoadPolicy));
-  }
-  // Places past w hold the next bucket's elements: -inf takes them out of
-  // every comparison below (the inputs are finite).
-  if (w < W) {
-#pragma unroll
-    for (int j = 0; j < W; ++j) v[j] = j < w ? v[j] : -__builtin_inff();
-  }
   // Column of the bucket's first element within the input row.
   const uint32_t b = static_cast<uint32_t>(a.buckets);
   const uint32_t r0 = g0 < 0x100000000LL ? static_cast<uint32_t>(g0) % b
@@ -295,11 +229,138 @@ __global__ __launch_bounds__((lane_waves<W, VEC>() * kWave)) void bucket_lanes(S
       }
       float x;
       if constexpr (kStage)
-        x = reinterpret_cast<const float*>(stage)[lane * kStride + col];
+        x = row[col];
       else
         x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, base + col * 4, 0, 0));
       put(i, x, static_cast<uint32_t>(col));
     }
+  }
+}
+
+// Waves per block: one, so that a block's LDS (17 KB for the 64-column
+// stage) frees as soon as its wave ends (measured 1-2% faster than four
+// waves for 8 and 32 buckets of 256 columns, 7% for 4 buckets).
+constexpr int kLaneWaves = 1;
+
+// Staged groups: each wave takes groups blockIdx.x, blockIdx.x + gridDim.x,
+// ... (the host sizes the grid to what is resident, never more than the
+// groups there are). The loads of a wave's next group are issued into
+// registers before the current group's selection, so every wave keeps a
+// group's loads in flight while it works; with one group per wave the
+// loads of a wave waited behind its own selection and the 9 waves per CU
+// that the LDS allows left the memory system idle part of the time.
+template <int W>
+__device__ __forceinline__ void load_group(const SelectArgs& a, int64_t g0, int live, int lane,
+                                           u32x4 (&q)[W / 4]) {
+  const int w = a.m;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a.x + g0 * w), 0, live * w * 4, kRsrcWord3);
+  // Chunk c = 64 i + lane (16 bytes) is place 4 (c mod (W/4)) of bucket
+  // c / (W/4); chunks past the group's buckets read zeros and are not
+  // written to LDS below.
+  constexpr int kChunks = W / 4;  // chunks per bucket
+#pragma unroll
+  for (int i = 0; i < W / 4; ++i) {
+    const int c = i * kWave + lane;
+    const int bkt = c / kChunks;
+    const int p = 4 * (c % kChunks);
+    q[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, (bkt * w + p) * 4, 0, kLoadPolicy);
+  }
+}
+
+template <int W, int KB, bool VEC, typename IdxT>
+__global__ __launch_bounds__(kLaneWaves * kWave) void bucket_lanes(SelectArgs a) {
+  constexpr bool kStage = lane_stage<W, VEC>();
+  const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+  const int w = a.m;
+  if constexpr (kStage) {
+    // LDS row of a lane: W + 4 floats (16-byte aligned; the skew of 4 banks
+    // per row keeps 8 consecutive lanes on distinct banks for both the
+    // writes and the reads below).
+    constexpr int kStride = W + 4;
+    constexpr int kChunks = W / 4;
+    __shared__ u32x4 stage[kWave * kStride / 4];
+    const int64_t groups = (a.n + kWave - 1) / kWave;
+    int64_t grp = blockIdx.x;
+    if (grp >= groups) return;
+    auto live_of = [&](int64_t g) {
+      const int64_t rest = a.n - g * kWave;
+      return rest < kWave ? static_cast<int>(rest) : kWave;
+    };
+    u32x4 q[W / 4];
+    load_group<W>(a, grp * kWave, live_of(grp), lane, q);
+    for (;;) {
+      const int64_t g0 = grp * kWave;
+      const int live = live_of(grp);
+#pragma unroll
+      for (int i = 0; i < W / 4; ++i) {
+        const int c = i * kWave + lane;
+        const int bkt = c / kChunks;
+        const int p = 4 * (c % kChunks);
+        if (p < w && bkt < live) stage[(bkt * kStride + p) / 4] = q[i];
+      }
+      // LDS operations of one wave complete in issue order; the barriers
+      // keep the compiler from moving the reads above the writes (and, at
+      // the loop's end, the next group's writes above this group's reads).
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
+      const int64_t next = grp + gridDim.x;
+      if (next < groups) load_group<W>(a, next * kWave, live_of(next), lane, q);
+      float v[W];
+#pragma unroll
+      for (int j = 0; j < W; j += 4) {
+        const u32x4 e = stage[(lane * kStride + j) / 4];
+        v[j] = __uint_as_float(e.x);
+        v[j + 1] = __uint_as_float(e.y);
+        v[j + 2] = __uint_as_float(e.z);
+        v[j + 3] = __uint_as_float(e.w);
+      }
+      // Places past w hold the next bucket's elements: -inf takes them out
+      // of every comparison (the inputs are finite).
+      if (w < W) {
+#pragma unroll
+        for (int j = 0; j < W; ++j) v[j] = j < w ? v[j] : -__builtin_inff();
+      }
+      const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(a.x), 0, 0, kRsrcWord3);
+      select_bucket<W, KB, true, IdxT>(a, g0, live, lane, v,
+                                       reinterpret_cast<const float*>(stage) + lane * kStride,
+                                       none, 0);
+      if (next >= groups) break;
+      grp = next;
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
+    }
+  } else {
+    const int64_t g0 = static_cast<int64_t>(blockIdx.x) * kWave;
+    if (g0 >= a.n) return;
+    const int live = a.n - g0 < kWave ? static_cast<int>(a.n - g0) : kWave;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.x + g0 * w), 0, live * w * 4, kRsrcWord3);
+    // Elements past the bucket (j >= w) belong to the next one and are
+    // never considered.
+    const int base = lane * w * 4;
+    float v[W];
+    if constexpr (VEC) {
+#pragma unroll
+      for (int j = 0; j < W; j += 4) {
+        const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(rx, base + j * 4, 0, kLoadPolicy);
+        v[j] = __uint_as_float(q.x);
+        v[j + 1] = __uint_as_float(q.y);
+        v[j + 2] = __uint_as_float(q.z);
+        v[j + 3] = __uint_as_float(q.w);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < W; ++j)
+        v[j] = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(rx, base + j * 4, 0, kLoadPolicy));
+    }
+    if (w < W) {
+#pragma unroll
+      for (int j = 0; j < W; ++j) v[j] = j < w ? v[j] : -__builtin_inff();
+    }
+    select_bucket<W, KB, false, IdxT>(a, g0, live, lane, v, nullptr, rx, base);
   }
 }
 
@@ -336,9 +397,18 @@ hipError_t launch_bucket_lanes(const SelectArgs& a, bool u8_index,
   const bool vec = a.m % 4 == 0 && (reinterpret_cast<uintptr_t>(a.x) & 15u) == 0;
   const RowsKernel fn =
       u8_index ? pick<uint8_t>(a.m, a.k, vec) : pick<int32_t>(a.m, a.k, vec);
-  // Must match lane_waves() for the kernel picked.
-  const int threads = kWave;
-  const int64_t blocks = (a.n + threads - 1) / threads;
+  const int threads = kLaneWaves * kWave;
+  int64_t blocks = (a.n + threads - 1) / threads;
+  // Staged groups (16-byte loads, buckets of more than 16 columns): a
+  // persistent grid of what is resident; the waves loop over the groups.
+  if (vec && a.m > 16 && blocks > 0) {
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return hipErrorInvalidDevice;
+    const int64_t resident =
+        static_cast<int64_t>(cu_count(device)) *
+        resident_blocks(reinterpret_cast<const void*>(fn), threads, device);
+    blocks = blocks < resident ? blocks : resident;
+  }
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(fn, dim3(static_cast<uint32_t>(blocks)), dim3(threads), 0,
                      stream, a);

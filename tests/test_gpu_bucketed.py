@@ -78,10 +78,11 @@ def test_bucketed_ragged_row_counts():
         assert_identical(gpu_bucketed(x, 32, 8, u8=True), oracle.bucketed(x, 32, 8), f"n={n}")
 
 
-def test_bucketed_full_shape():
+@pytest.mark.parametrize("b", [8, 4, 2])
+def test_bucketed_full_shape(b):
     x = workloads.config_input(3, 262144, 256)
-    assert_identical(gpu_bucketed(x, 32, 8, u8=True), oracle.bucketed(x, 32, 8),
-                     "262144 x 256 k=32 b=8")
+    assert_identical(gpu_bucketed(x, 32, b, u8=True), oracle.bucketed(x, 32, b),
+                     f"262144 x 256 k=32 b={b}")
 
 
 @pytest.mark.parametrize("m,k,b", [(256, 32, 8), (96, 12, 4), (64, 16, 16), (256, 32, 4)])

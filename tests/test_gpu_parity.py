@@ -328,3 +328,17 @@ def test_short_rows_many_per_wave(m):
     xt = buf[1:].view(777, m)
     for k in sorted({1, 4, 8} & set(range(1, m + 1))):
         assert_identical(gpu_run_t(xt, k, "exact"), oracle.exact(x, k), f"short misaligned M={m}")
+
+
+# Batches larger than one resident grid: each wave of the staged lane kernel
+# loops over several groups of 64 rows, loading the next group while it
+# selects the current one; the row counts end inside a group. Normal and
+# tie-heavy rows (quarter steps, about 30 distinct values).
+@pytest.mark.parametrize("n,m,k", [(2097152 + 5, 32, 4), (1048576 + 37, 64, 8),
+                                   (600001, 48, 6), (700003, 20, 3), (500009, 64, 1)])
+def test_short_rows_beyond_resident_grid(n, m, k):
+    x = workloads.normal(n, m, seed=n % 1000)
+    check(x, k, "exact", u8=True, label=f"short n={n} M={m}")
+    xq = np.round(x[: n // 2] * 4) / 4 + np.float32(0.0)
+    check(np.ascontiguousarray(xq.astype(np.float32)), k, "exact",
+          label=f"short ties n={n // 2} M={m}")
