@@ -40,6 +40,7 @@ FAMILY_SOURCES = {
     "rows_in_registers": ["rtopk_rows.hpp"],
     "rows_in_group": ["rtopk_rows.hpp", "rtopk_group.hpp"],
     "bucket_lanes": ["rtopk_bucket.hip"],
+    "bucket_pairs": ["rtopk_bucket.hip"],
     "scatter_rows": ["rtopk_maxk.hip"],
     "spgemm_rows": ["rtopk_spgemm.hip"],
     "sspmm_rows": ["rtopk_spgemm.hip"],
@@ -161,6 +162,17 @@ def workload_name(args) -> str:
             + f" idx={args.index}")
 
 
+def _short_kernel(width: int, kb: int):
+    """Kernel of the library's short rows (or buckets) of `width` columns
+    keeping `kb` (inputs 16-byte aligned, as bench.py allocates them), if
+    they take one."""
+    if width <= 64 and kb <= 8:
+        return "bucket_lanes"
+    if width <= 128 and kb <= 16 and width % 4 == 0:
+        return "bucket_pairs"
+    return None
+
+
 def op_kernel(args) -> str:
     """Name fragment of the kernel the op's counters are attributed to, as the
     library routes the workload (specific enough to leave out the exact
@@ -172,7 +184,7 @@ def op_kernel(args) -> str:
         return f"{args.op}_rows"
     if args.op == "bucketed":
         width, kb = args.m // args.buckets, args.k // args.buckets
-        return "bucket_lanes" if width <= 64 and kb <= 8 else "(rtopk::Mode)3"
+        return _short_kernel(width, kb) or "(rtopk::Mode)3"
     if args.op == "maxk_forward":
         if args.m <= 1024:
             return "(rtopk::Mode)2"
@@ -182,8 +194,9 @@ def op_kernel(args) -> str:
                                      and getattr(args, "eps", 1.0) == 0.0)
     if not exact:
         return "(rtopk::Mode)0"
-    if args.m <= 64 and args.k <= 8:
-        return "bucket_lanes"
+    short = _short_kernel(args.m, args.k)
+    if short:
+        return short
     if args.m > 4096 and index != "u8":
         return "rows_in_group"
     return "(rtopk::Mode)1"

@@ -31,12 +31,12 @@ rtopk_status_t run(const float* x, int64_t n, int32_t m, int32_t k,
   if (st != RTOPK_SUCCESS) return st;
   if (n == 0) return RTOPK_SUCCESS;
   rtopk::SelectArgs a{x, n, m, k, max_iter, eps, out_val, out_idx, 0.0f, 0.0f, nullptr, 1};
-  // Short rows keeping few survivors, exact: one lane per row, 64 rows per
-  // wave (the bucket kernel with one bucket per row), instead of one row per
-  // wave with most lanes idle.
+  // Short rows keeping few survivors, exact: one lane (or two) per row, 64
+  // (or 32) rows per wave (the bucket kernels with one bucket per row),
+  // instead of one row per wave with most lanes idle.
   const bool exact = mode == rtopk::Mode::kExact ||
                      (mode == rtopk::Mode::kCapped && max_iter < 0 && eps == 0.0f);
-  const hipError_t err = exact && rtopk::bucket_lanes_supported(m, k)
+  const hipError_t err = exact && rtopk::bucket_lanes_supported(x, m, k)
                              ? rtopk::launch_bucket_lanes(a, u8_index, stream)
                              : rtopk::launch_select(a, mode, u8_index, stream);
   return err == hipSuccess ? RTOPK_SUCCESS : RTOPK_ERROR_LAUNCH;
@@ -103,7 +103,7 @@ rtopk_status_t run_bucketed(const float* x, int64_t n, int32_t m, int32_t k,
   rtopk::SelectArgs a{x,       n * buckets, width, k / buckets, -1, 0.0f,
                       out_val, out_idx,     0.0f,  0.0f,        nullptr, buckets};
   const hipError_t err =
-      rtopk::bucket_lanes_supported(width, k / buckets)
+      rtopk::bucket_lanes_supported(x, width, k / buckets)
           ? rtopk::launch_bucket_lanes(a, u8_index, stream)
           : rtopk::launch_select(a, rtopk::Mode::kBucket, u8_index, stream);
   return err == hipSuccess ? RTOPK_SUCCESS : RTOPK_ERROR_LAUNCH;

@@ -13,7 +13,8 @@
 // by median-of-three insertion, then one pass in column order that keeps
 // every element above the kb-th largest value and the first few equal to
 // it. A wave takes 64 consecutive buckets, so its loads and stores cover
-// one contiguous stretch of the input and of the outputs.
+// one contiguous stretch of the input and of the outputs. Buckets of 65 to
+// 128 columns keeping at most 16 take two lanes each (bucket_pairs below).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -33,14 +34,19 @@ constexpr int kLoadPolicy = 0;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// acc = 2 * acc + (x >= t), and the same with x == t: the compare's lane
-// mask is the carry-in of one add (two instructions, no mask logic).
-__device__ __forceinline__ void shift_in_ge(uint32_t& acc, float x, float t) {
-  asm("v_cmp_le_f32 vcc, %2, %1\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc"
-      : "+v"(acc)
-      : "v"(x), "v"(t)
-      : "vcc");
+// acc = 2 * acc + (x < t), from the sign of x - t: for finite x and t the
+// difference is rounded once, so it is negative exactly when x < t, except
+// that -0 - (+0) is -0. Callers pass a zero threshold as -0 (see
+// zero_as_minus), and x - (-0) is +0 for x = +-0. One subtraction and one
+// funnel shift per place, with no lane mask.
+__device__ __forceinline__ uint32_t shift_in_lt(uint32_t acc, float x, float t) {
+  return (acc << 1) | (__float_as_uint(x - t) >> 31);
 }
+__device__ __forceinline__ float zero_as_minus(float t) {
+  return __uint_as_float(t == 0.0f ? 0x80000000u : __float_as_uint(t));
+}
+// acc = 2 * acc + (x == t): the compare's lane mask is the carry-in of one
+// add (two instructions, no mask logic).
 __device__ __forceinline__ void shift_in_eq(uint32_t& acc, float x, float t) {
   asm("v_cmp_eq_f32 vcc, %2, %1\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc"
       : "+v"(acc)
@@ -170,19 +176,19 @@ __device__ __forceinline__ void select_bucket(const SelectArgs& a, int64_t g0, i
 #pragma unroll
     for (int i = 0; i < KB; ++i) need_eq += (i < kb && tv[i] == thr) ? 1 : 0;
     // Bit masks of the places at or above thr: place j at bit 31 - (j mod
-    // 32) of word j / 32 (a mask doubles and takes the new bit: one
-    // shift-add per place, no lane-mask logic). Without surplus ties these
-    // are the survivors.
+    // 32) of word j / 32 (built from the places below thr). Without surplus
+    // ties these are the survivors.
     constexpr int NW = (W + 31) / 32;
     uint32_t keep[NW];
     int count = 0;
+    const float thr_s = zero_as_minus(thr);
 #pragma unroll
     for (int q = 0; q < NW; ++q) {
       constexpr int kLast = W < 32 ? W : 32;  // places per word
-      keep[q] = 0;
+      uint32_t below = 0;
 #pragma unroll
-      for (int j = 0; j < kLast; ++j) shift_in_ge(keep[q], v[32 * q + j], thr);
-      keep[q] <<= 32 - kLast;
+      for (int j = 0; j < kLast; ++j) below = shift_in_lt(below, v[32 * q + j], thr_s);
+      keep[q] = ~below << (32 - kLast);
       count += __builtin_popcount(keep[q]);
     }
     if (__builtin_amdgcn_ballot_w64(count > kb) != 0) {
@@ -212,9 +218,12 @@ __device__ __forceinline__ void select_bucket(const SelectArgs& a, int64_t g0, i
         }
       }
     }
-    // Emit them lowest column first. The value is read again from the
-    // bucket (from LDS, or from its line in the cache), which keeps the
-    // original bits.
+    // Emit them lowest column first: the columns, then the values (read
+    // again from the bucket, from LDS or from its line in the cache, which
+    // keeps the original bits; the reads are issued together), then the
+    // stores, as straight-line code (a branch between survivors made each
+    // read wait by itself).
+    int cols[KB];
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
       int col = 0;
@@ -227,13 +236,19 @@ __device__ __forceinline__ void select_bucket(const SelectArgs& a, int64_t g0, i
         keep[q] &= here ? ~(0x80000000u >> c) : ~0u;
         found = found || here;
       }
-      float x;
-      if constexpr (kStage)
-        x = row[col];
-      else
-        x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, base + col * 4, 0, 0));
-      put(i, x, static_cast<uint32_t>(col));
+      cols[i] = col;
     }
+    float xs[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      if constexpr (kStage)
+        xs[i] = row[cols[i]];
+      else
+        xs[i] = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(rx, base + cols[i] * 4, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < KB; ++i) put(i, xs[i], static_cast<uint32_t>(cols[i]));
   }
 }
 
@@ -241,6 +256,7 @@ __device__ __forceinline__ void select_bucket(const SelectArgs& a, int64_t g0, i
 // stage) frees as soon as its wave ends (measured 1-2% faster than four
 // waves for 8 and 32 buckets of 256 columns, 7% for 4 buckets).
 constexpr int kLaneWaves = 1;
+constexpr int kSimdsPerCu = 4;
 
 // Staged groups: each wave takes groups blockIdx.x, blockIdx.x + gridDim.x,
 // ... (the host sizes the grid to what is resident, never more than the
@@ -289,6 +305,14 @@ __global__ __launch_bounds__(kLaneWaves * kWave) void bucket_lanes(SelectArgs a)
     };
     u32x4 q[W / 4];
     load_group<W>(a, grp * kWave, live_of(grp), lane, q);
+    // Places past w of every LDS row hold -inf for the whole kernel (the
+    // staging below writes places < w only), which takes them out of every
+    // comparison (the inputs are finite). Written after the first loads
+    // are issued, so that they do not wait behind it.
+    if (w < W) {
+      constexpr u32x4 kNegInf = {0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u};
+      for (int i = lane; i < kWave * kStride / 4; i += kWave) stage[i] = kNegInf;
+    }
     for (;;) {
       const int64_t g0 = grp * kWave;
       const int live = live_of(grp);
@@ -314,12 +338,6 @@ __global__ __launch_bounds__(kLaneWaves * kWave) void bucket_lanes(SelectArgs a)
         v[j + 1] = __uint_as_float(e.y);
         v[j + 2] = __uint_as_float(e.z);
         v[j + 3] = __uint_as_float(e.w);
-      }
-      // Places past w hold the next bucket's elements: -inf takes them out
-      // of every comparison (the inputs are finite).
-      if (w < W) {
-#pragma unroll
-        for (int j = 0; j < W; ++j) v[j] = j < w ? v[j] : -__builtin_inff();
       }
       const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<float*>(a.x), 0, 0, kRsrcWord3);
@@ -364,6 +382,236 @@ __global__ __launch_bounds__(kLaneWaves * kWave) void bucket_lanes(SelectArgs a)
   }
 }
 
+// Buckets of 65 to 128 columns keeping at most 16 (w a multiple of 4, x
+// 16-byte aligned): two lanes per bucket, lane l taking bucket l mod 32 of
+// a group of 32 and its half l / 32 (columns [64h, 64h + 64)). Each lane
+// finds the KB largest values of its half by median-of-three insertion;
+// the two sorted lists are exchanged between lanes l and l ^ 32 and merged
+// (the elementwise maximum of one list and the other reversed holds the KB
+// largest of both, as a bitonic sequence, which a half-cleaner network
+// sorts), so both lanes hold the bucket's KB largest values. Each lane then
+// keeps its places at or above the kb-th of them; surplus ties at that
+// value are dropped from the highest columns (the low half keeps its equal
+// places first). The low half emits its survivors first, the high half
+// after them, so the bucket's entries are in column order. Persistent grid
+// and staging as in bucket_lanes: the next group's loads are in flight
+// while the current group is selected.
+constexpr int kPairWidth = kPairBucketWidth;  // bucket capacity (two halves of 64)
+constexpr int kPairGroup = kWave / 2;  // buckets per group
+
+template <int KB, typename IdxT>
+__global__ __launch_bounds__(kWave) void bucket_pairs(SelectArgs a) {
+  constexpr int kHalf = kPairWidth / 2;
+  constexpr int kStride = kPairWidth + 4;  // LDS floats per bucket
+  constexpr int kChunks = kPairWidth / 4;  // 16-byte chunks per bucket
+  constexpr int kLoads = kPairGroup * kChunks / kWave;  // chunks per lane
+  __shared__ u32x4 stage[kPairGroup * kStride / 4];
+  const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+  const int bl = lane & (kPairGroup - 1);  // bucket within the group
+  const int h = lane / kPairGroup;         // half
+  const int partner = (lane ^ kPairGroup) << 2;  // ds_bpermute address
+  const int w = a.m, kb = a.k;
+  const int64_t groups = (a.n + kPairGroup - 1) / kPairGroup;
+  int64_t grp = blockIdx.x;
+  if (grp >= groups) return;
+  auto live_of = [&](int64_t g) {
+    const int64_t rest = a.n - g * kPairGroup;
+    return rest < kPairGroup ? static_cast<int>(rest) : kPairGroup;
+  };
+  // Chunk c = 64 i + lane (16 bytes) is place 4 (c mod 32) of bucket c / 32
+  // of the group; chunks past the group's buckets read zeros and chunks
+  // past a bucket (w < 128) belong to the next one: neither is written to
+  // LDS below.
+  auto load = [&](int64_t g, u32x4 (&q)[kLoads]) {
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.x + g * kPairGroup * w), 0, live_of(g) * w * 4, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int c = i * kWave + lane;
+      q[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rx, ((c / kChunks) * w + 4 * (c % kChunks)) * 4, 0, kLoadPolicy);
+    }
+  };
+  u32x4 q[kLoads];
+  load(grp, q);
+  // Places past w of every LDS bucket row hold -inf for the whole kernel
+  // (the staging below writes places < w only), which takes them out of
+  // every comparison (the inputs are finite). Written after the first
+  // loads are issued, so that they do not wait behind it.
+  if (w < kPairWidth) {
+    constexpr u32x4 kNegInf = {0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u};
+    for (int i = lane; i < kPairGroup * kStride / 4; i += kWave) stage[i] = kNegInf;
+  }
+  const uint32_t nb = static_cast<uint32_t>(a.buckets);
+  for (;;) {
+    const int64_t g0 = grp * kPairGroup;
+    const int live = live_of(grp);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int c = i * kWave + lane;
+      const int bkt = c / kChunks;
+      const int p = 4 * (c % kChunks);
+      if (p < w && bkt < live) stage[(bkt * kStride + p) / 4] = q[i];
+    }
+    // LDS operations of one wave complete in issue order; the barriers keep
+    // the compiler from moving the reads above the writes (and, at the
+    // loop's end, the next group's writes above this group's reads).
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    const int64_t next = grp + gridDim.x;
+    if (next < groups) load(next, q);
+    const float* row = reinterpret_cast<const float*>(stage) + bl * kStride + kHalf * h;
+    float v[kHalf];
+#pragma unroll
+    for (int j = 0; j < kHalf; j += 4) {
+      const u32x4 e = *reinterpret_cast<const u32x4*>(row + j);
+      v[j] = __uint_as_float(e.x);
+      v[j + 1] = __uint_as_float(e.y);
+      v[j + 2] = __uint_as_float(e.z);
+      v[j + 3] = __uint_as_float(e.w);
+    }
+    // The KB largest values of the half, largest first.
+    float tv[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) tv[i] = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < kHalf; ++j) {
+      const float x = v[j];
+#pragma unroll
+      for (int i = KB - 1; i > 0; --i) tv[i] = __builtin_amdgcn_fmed3f(tv[i - 1], x, tv[i]);
+      tv[0] = fmaxf(tv[0], x);
+    }
+    // Merge with the other half's list: c[i] = max(tv[i], other[KB-1-i]),
+    // then sort the bitonic sequence (half-cleaners at distance KB/2 .. 1).
+    float cv[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const float o = __int_as_float(
+          __builtin_amdgcn_ds_bpermute(partner, __float_as_int(tv[KB - 1 - i])));
+      cv[i] = fmaxf(tv[i], o);
+    }
+#pragma unroll
+    for (int d = KB / 2; d >= 1; d /= 2) {
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        if ((i & d) == 0) {
+          const float hi = fmaxf(cv[i], cv[i + d]);
+          const float lo = fminf(cv[i], cv[i + d]);
+          cv[i] = hi;
+          cv[i + d] = lo;
+        }
+      }
+    }
+    // The kb-th largest value of the bucket and how many of the kb largest
+    // equal it.
+    float thr = cv[0];
+#pragma unroll
+    for (int i = 1; i < KB; ++i) thr = i < kb ? cv[i] : thr;
+    int need_eq = 0;
+#pragma unroll
+    for (int i = 0; i < KB; ++i) need_eq += (i < kb && cv[i] == thr) ? 1 : 0;
+    // Places of the half at or above thr: place j at bit 31 - (j mod 32)
+    // of word j / 32.
+    uint32_t keep[2];
+    int count = 0;
+    const float thr_s = zero_as_minus(thr);
+#pragma unroll
+    for (int qw = 0; qw < 2; ++qw) {
+      uint32_t below = 0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) below = shift_in_lt(below, v[32 * qw + j], thr_s);
+      keep[qw] = ~below;
+      count += __builtin_popcount(keep[qw]);
+    }
+    const int count_other = __builtin_amdgcn_ds_bpermute(partner, count);
+    if (__builtin_amdgcn_ballot_w64(count + count_other > kb) != 0) {
+      // Surplus ties at thr: keep every place above it and the need_eq
+      // lowest-column places equal to it, low half first.
+      uint32_t equal[2];
+      int eq = 0;
+#pragma unroll
+      for (int qw = 0; qw < 2; ++qw) {
+        equal[qw] = 0;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) shift_in_eq(equal[qw], v[32 * qw + j], thr);
+        keep[qw] &= ~equal[qw];
+        eq += __builtin_popcount(equal[qw]);
+      }
+      const int eq_other = __builtin_amdgcn_ds_bpermute(partner, eq);
+      const int quota = h == 0 ? need_eq : need_eq - (eq_other < need_eq ? eq_other : need_eq);
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        bool done = i >= quota;
+#pragma unroll
+        for (int qw = 0; qw < 2; ++qw) {
+          const uint32_t top = equal[qw] != 0u ? 0x80000000u >> __builtin_clz(equal[qw]) : 0u;
+          const bool take = !done && top != 0u;
+          keep[qw] |= take ? top : 0u;
+          equal[qw] ^= take ? top : 0u;
+          done = done || take;
+        }
+      }
+      count = __builtin_popcount(keep[0]) + __builtin_popcount(keep[1]);
+    }
+    // The high half's entries follow the low half's. The exchange runs on
+    // every lane: a permute evaluated only where h == 1 would read the low
+    // half's lanes while they are inactive, which yields 0.
+    const int count_low = __builtin_amdgcn_ds_bpermute(partner, count);
+    const int base = h == 0 ? 0 : count_low;
+    const uint32_t r0 = g0 < 0x100000000LL ? static_cast<uint32_t>(g0) % nb
+                                           : static_cast<uint32_t>(g0 % a.buckets);
+    const uint32_t first =
+        ((r0 + static_cast<uint32_t>(bl)) % nb) * static_cast<uint32_t>(w) + kHalf * h;
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        a.out_val + g0 * kb, 0, live * kb * 4, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<IdxT*>(a.out_idx) + g0 * kb, 0,
+        live * kb * static_cast<int>(sizeof(IdxT)), kRsrcWord3);
+    // Columns of the lane's survivors, lowest first; then their values (the
+    // LDS reads issued together rather than one wait per survivor); then
+    // the stores. Entries past the lane's survivors store past the
+    // resources' end, where the hardware drops them.
+    int cols[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      int col = 0;
+      bool found = false;
+#pragma unroll
+      for (int qw = 0; qw < 2; ++qw) {
+        const bool here = !found && keep[qw] != 0u;
+        const int c = keep[qw] != 0u ? __builtin_clz(keep[qw]) : 0;
+        col = here ? 32 * qw + c : col;
+        keep[qw] &= here ? ~(0x80000000u >> c) : ~0u;
+        found = found || here;
+      }
+      cols[i] = col;
+    }
+    uint32_t xs[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) xs[i] = __float_as_uint(row[cols[i]]);
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const int e = i < count ? bl * kb + base + i : (1 << 28);
+      __builtin_amdgcn_raw_buffer_store_b32(xs[i], rv, e * 4, 0, 0);
+      if constexpr (sizeof(IdxT) == 1)
+        __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(first + cols[i]), ri, e, 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b32(first + cols[i], ri, e * 4, 0, 0);
+    }
+    if (next >= groups) break;
+    grp = next;
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+  }
+}
+
+template <typename IdxT>
+RowsKernel pick_pair(int kb) {
+  if (kb <= 4) return bucket_pairs<4, IdxT>;
+  if (kb <= 8) return bucket_pairs<8, IdxT>;
+  return bucket_pairs<16, IdxT>;
+}
+
 template <int W, bool VEC, typename IdxT>
 RowsKernel pick_kb(int kb) {
   if (kb <= 1) return bucket_lanes<W, 1, VEC, IdxT>;
@@ -387,26 +635,37 @@ RowsKernel pick(int w, int kb, bool vec) {
 
 }  // namespace bucket_detail
 
-bool bucket_lanes_supported(int width, int kb) {
-  return width <= kLaneBucketWidth && kb <= kLaneBucketSurvivors;
+bool bucket_lanes_supported(const float* x, int width, int kb) {
+  if (width <= kLaneBucketWidth) return kb <= kLaneBucketSurvivors;
+  return width <= kPairBucketWidth && kb <= kPairBucketSurvivors && width % 4 == 0 &&
+         (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
 }
 
 hipError_t launch_bucket_lanes(const SelectArgs& a, bool u8_index,
                                hipStream_t stream) {
   using namespace bucket_detail;
   const bool vec = a.m % 4 == 0 && (reinterpret_cast<uintptr_t>(a.x) & 15u) == 0;
-  const RowsKernel fn =
-      u8_index ? pick<uint8_t>(a.m, a.k, vec) : pick<int32_t>(a.m, a.k, vec);
+  const bool pairs = a.m > kLaneBucketWidth;
+  if (pairs && (!vec || a.m > kPairWidth || a.k > kPairBucketSurvivors))
+    return hipErrorInvalidValue;
+  const RowsKernel fn = pairs ? (u8_index ? pick_pair<uint8_t>(a.k) : pick_pair<int32_t>(a.k))
+                              : (u8_index ? pick<uint8_t>(a.m, a.k, vec)
+                                          : pick<int32_t>(a.m, a.k, vec));
   const int threads = kLaneWaves * kWave;
-  int64_t blocks = (a.n + threads - 1) / threads;
+  const int per_block = pairs ? kPairGroup : threads;
+  int64_t blocks = (a.n + per_block - 1) / per_block;
   // Staged groups (16-byte loads, buckets of more than 16 columns): a
   // persistent grid of what is resident; the waves loop over the groups.
+  // Every wave gets the same share of groups, so the single-wave blocks per
+  // CU are rounded down to a multiple of the CU's four SIMDs: with 17 (the
+  // LDS limit of the 32-column kernel) one SIMD ran five waves, and the
+  // whole launch waited for it (measured 3% slower than 16).
   if (vec && a.m > 16 && blocks > 0) {
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return hipErrorInvalidDevice;
-    const int64_t resident =
-        static_cast<int64_t>(cu_count(device)) *
-        resident_blocks(reinterpret_cast<const void*>(fn), threads, device);
+    int per_cu = resident_blocks(reinterpret_cast<const void*>(fn), threads, device);
+    if (per_cu >= kSimdsPerCu) per_cu -= per_cu % kSimdsPerCu;
+    const int64_t resident = static_cast<int64_t>(cu_count(device)) * per_cu;
     blocks = blocks < resident ? blocks : resident;
   }
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;

@@ -191,13 +191,18 @@ hipError_t launch_spgemm(SpgemmArgs a, bool u8_index, hipStream_t stream);
 // ([n_src, k], zeroed, then accumulated).
 hipError_t launch_sspmm(SpgemmArgs a, bool u8_index, hipStream_t stream);
 
-// Bucketed top-k with short buckets (rtopk_bucket.hip): one lane per bucket,
+// Bucketed top-k with short buckets (rtopk_bucket.hip): one lane per bucket
 // for buckets of at most kLaneBucketWidth columns keeping at most
-// kLaneBucketSurvivors each. `a` is the bucket view (n = rows * buckets,
-// m = bucket width, k = survivors per bucket, buckets = buckets per row).
+// kLaneBucketSurvivors each; two lanes per bucket for buckets of up to
+// kPairBucketWidth columns keeping at most kPairBucketSurvivors, where the
+// width is a multiple of 4 and x is 16-byte aligned. `a` is the bucket view
+// (n = rows * buckets, m = bucket width, k = survivors per bucket, buckets
+// = buckets per row).
 constexpr int kLaneBucketWidth = 64;
 constexpr int kLaneBucketSurvivors = 8;
-bool bucket_lanes_supported(int width, int kb);
+constexpr int kPairBucketWidth = 128;
+constexpr int kPairBucketSurvivors = 16;
+bool bucket_lanes_supported(const float* x, int width, int kb);
 hipError_t launch_bucket_lanes(const SelectArgs& a, bool u8_index,
                                hipStream_t stream);
 

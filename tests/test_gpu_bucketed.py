@@ -44,6 +44,12 @@ CASES = [  # (n, m, k, buckets)
     (81, 96, 12, 4), (70, 2048, 512, 64), (66, 8192, 256, 256),
     (120, 256, 32, 4), (90, 200, 20, 4), (77, 96, 8, 2), (60, 128, 2, 2),
     (45, 132, 24, 3),
+    # Buckets of 65 to 128 columns keeping at most 16 (two lanes per bucket,
+    # 32 buckets per wave) where the width is a multiple of 4; other widths
+    # take the wave kernel.
+    (257, 256, 32, 2), (300, 200, 10, 2), (130, 272, 24, 4), (99, 340, 20, 4),
+    (65, 384, 12, 3), (70, 248, 2, 2), (1000, 256, 16, 2), (31, 256, 30, 2),
+    (33, 136, 32, 2), (47, 512, 64, 4),
 ]
 
 
@@ -85,7 +91,8 @@ def test_bucketed_full_shape(b):
                      f"262144 x 256 k=32 b={b}")
 
 
-@pytest.mark.parametrize("m,k,b", [(256, 32, 8), (96, 12, 4), (64, 16, 16), (256, 32, 4)])
+@pytest.mark.parametrize("m,k,b", [(256, 32, 8), (96, 12, 4), (64, 16, 16), (256, 32, 4),
+                                   (256, 32, 2)])
 def test_bucketed_unaligned_input(m, k, b):
     # A matrix starting one float past a 16-byte boundary: the short-bucket
     # kernel then reads with 4-byte loads.

@@ -300,15 +300,18 @@ def test_nonnull_stream():
     assert_identical((v.cpu().numpy(), i.cpu().numpy()), oracle.exact(x_np, 32), "stream")
 
 
-# Short rows with few survivors take one lane per row (64 rows per wave):
-# row lengths around the 8/16/32/64-column classes, every survivor class,
+# Short rows with few survivors take one lane per row (64 rows per wave), or
+# two (32 rows per wave) for 65 to 128 columns keeping at most 16: row
+# lengths around the 8/16/32/64/128-column classes, every survivor class,
 # row counts that end inside a wave, tie-heavy and adversarial rows, and an
-# input that starts one float past a 16-byte boundary (4-byte loads).
-@pytest.mark.parametrize("m", [1, 3, 8, 9, 16, 17, 31, 32, 33, 63, 64])
+# input that starts one float past a 16-byte boundary (4-byte loads; the
+# 65-128 column rows then take one wave per row).
+@pytest.mark.parametrize("m", [1, 3, 8, 9, 16, 17, 31, 32, 33, 63, 64, 65, 68, 96, 100, 124,
+                               127, 128])
 def test_short_rows_many_per_wave(m):
     rng = np.random.default_rng(500 + m)
-    for n in (1, 63, 64, 65, 1000, 4097):
-        for k in sorted({1, 2, 3, 5, 8} & set(range(1, m + 1))):
+    for n in (1, 31, 32, 33, 63, 64, 65, 1000, 4097):
+        for k in sorted({1, 2, 3, 5, 8, 9, 16} & set(range(1, m + 1))):
             fam = (n + k) % 3
             if fam == 0:
                 x = rng.standard_normal((n, m)).astype(np.float32)
@@ -326,7 +329,7 @@ def test_short_rows_many_per_wave(m):
     buf = torch.zeros(777 * m + 1, dtype=torch.float32, device=dev())
     buf[1:].copy_(torch.from_numpy(x.reshape(-1)))
     xt = buf[1:].view(777, m)
-    for k in sorted({1, 4, 8} & set(range(1, m + 1))):
+    for k in sorted({1, 4, 8, 16} & set(range(1, m + 1))):
         assert_identical(gpu_run_t(xt, k, "exact"), oracle.exact(x, k), f"short misaligned M={m}")
 
 
@@ -335,7 +338,9 @@ def test_short_rows_many_per_wave(m):
 # selects the current one; the row counts end inside a group. Normal and
 # tie-heavy rows (quarter steps, about 30 distinct values).
 @pytest.mark.parametrize("n,m,k", [(2097152 + 5, 32, 4), (1048576 + 37, 64, 8),
-                                   (600001, 48, 6), (700003, 20, 3), (500009, 64, 1)])
+                                   (600001, 48, 6), (700003, 20, 3), (500009, 64, 1),
+                                   (1048576 + 17, 128, 16), (600011, 100, 12),
+                                   (500009, 68, 5)])
 def test_short_rows_beyond_resident_grid(n, m, k):
     x = workloads.normal(n, m, seed=n % 1000)
     check(x, k, "exact", u8=True, label=f"short n={n} M={m}")
