@@ -155,7 +155,9 @@ def workload_name(args) -> str:
         return (f"bucketed {args.inputs} N={args.rows} M={args.m} k={args.k} "
                 f"buckets={args.buckets} idx={args.index}")
     if args.op in ("spgemm", "sspmm"):
-        return (f"{args.op} power-law graph N={args.rows} mean_degree={args.degree:g} "
+        src = "" if getattr(args, "src_rows", None) in (None, args.rows) else \
+            f" src_rows={args.src_rows}"
+        return (f"{args.op} power-law graph N={args.rows} mean_degree={args.degree:g}{src} "
                 f"M={args.m} k={args.k} idx={args.index}")
     return (f"{args.inputs} N={args.rows} M={args.m} k={args.k} {args.mode}"
             + ("" if args.mode == "exact" else f" max_iter={args.max_iter} eps={args.eps}")
@@ -218,6 +220,11 @@ def parse():
                         "150 launches (~10 ms) of sustained load to settle")
     p.add_argument("--degree", type=float, default=64.0,
                    help="mean degree of the power-law graph for --op spgemm")
+    p.add_argument("--src-rows", type=int, default=None,
+                   help="--op spgemm/sspmm: the graph's edges point into the first "
+                        "SRC_ROWS rows only (default: all rows). A smaller footprint "
+                        "stands for what one XCD would gather from if the edges were "
+                        "partitioned by source-row block")
     p.add_argument("--buckets", type=int, default=8,
                    help="buckets per row for --op bucketed")
     p.add_argument("--config", type=int, choices=sorted(CONFIGS), default=None,
@@ -320,7 +327,10 @@ def main():
         sel = rt.rtopk_select_exact_u8 if u8 else rt.rtopk_select_exact
         feats = [sel(xb, k) for xb in xs]
         del xs
-        rp_np, ci_np, va_np = workloads.power_law_graph(n, n, args.degree, 4096, seed=48)
+        n_src = n if args.src_rows is None else args.src_rows
+        if not 1 <= n_src <= n:
+            raise SystemExit("--src-rows must be between 1 and --rows")
+        rp_np, ci_np, va_np = workloads.power_law_graph(n, n_src, args.degree, 4096, seed=48)
         nnz = int(ci_np.shape[0])
         rp_t = torch.from_numpy(rp_np).to(dev)
         ci_t = torch.from_numpy(ci_np).to(dev)
@@ -435,7 +445,8 @@ def main():
         # row). The per-edge gathers of neighbour rows (nnz * k * (4 + b);
         # backward: index rows plus atomics) are served mostly by the caches
         # and reported separately.
-        per_row = 4 * m + k * (4 + idx_bytes) + 8 + (nnz * 8) / n
+        n_src = n if args.src_rows is None else args.src_rows
+        per_row = 4 * m + k * (4 + idx_bytes) * n_src / n + 8 + (nnz * 8) / n
         if args.op == "sspmm":
             per_row = 4 * m + k * (idx_bytes + 4) + 8 + (nnz * 8) / n
         gather = nnz * k * (4 + idx_bytes)

@@ -141,6 +141,11 @@ def test_named_configs_and_overrides(monkeypatch):
                                       "--max-iter", "4", "--eps", "1e-4"])
     a = bench.parse()
     assert (a.rows, a.k, a.max_iter, a.eps) == (65536, 32, 4, 1e-4)
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--op", "spgemm", "--src-rows", "32768"])
+    a = bench.parse()
+    assert "src_rows=32768" in bench.workload_name(a)
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--op", "spgemm"])
+    assert "src_rows" not in bench.workload_name(bench.parse())
 
 
 def test_source_hash_is_per_kernel():
