@@ -134,6 +134,32 @@ def test_out_of_range_edges_and_survivors_are_skipped():
     check(rp, ci, va, sd, si, m, "out of range")
 
 
+def test_unaligned_features():
+    # Features starting one float (one byte) past an aligned address: the
+    # kernel's per-lane loads must not assume more alignment than the
+    # element size.
+    import row_wise_top_amd as rt
+    n_src, m, k = 3000, 256, 32
+    rp, ci, va = workloads.power_law_graph(2500, n_src, 20.0, 400, seed=49)
+    sd, si = features(n_src, m, k, seed=50)
+    want, absum = oracle.spgemm(rp, ci, va, n_src, sd, si, m, return_absum=True)
+    d = torch.device("cuda:0")
+    deg = np.diff(rp).astype(np.float64)
+    tol = (deg[:, None] + 2.0) * 2.0 ** -24 * absum.astype(np.float64) + 2.0 ** -126
+    for shift in (0, 1):
+        bd = torch.zeros(n_src * k + 4, dtype=torch.float32, device=d)
+        bd[shift:shift + n_src * k].copy_(torch.from_numpy(sd.reshape(-1)))
+        bi = torch.zeros(n_src * k + 4, dtype=torch.uint8, device=d)
+        bi[shift:shift + n_src * k].copy_(torch.from_numpy(si.reshape(-1).astype(np.uint8)))
+        y = rt.rtopk_cbsr_spgemm(torch.from_numpy(rp).to(d), torch.from_numpy(ci).to(d),
+                                 torch.from_numpy(va).to(d),
+                                 bd[shift:shift + n_src * k].view(n_src, k),
+                                 bi[shift:shift + n_src * k].view(n_src, k), m)
+        torch.cuda.synchronize()
+        err = np.abs(y.cpu().numpy().astype(np.float64) - want.astype(np.float64))
+        assert np.all(err <= tol), f"shift {shift}"
+
+
 def test_full_size_graph():
     n, m, k = 262144, 256, 32
     rp, ci, va = workloads.power_law_graph(n, n, 64.0, 4096, seed=48)
