@@ -122,15 +122,20 @@ inline int exact_candidate_slots(int q, int k) {
 // Candidate slots of the capped search (see capped_row): the capped kernel
 // stages the elements above the exact search's first threshold (steered by
 // the exact search's model constants for this window) before its first
-// step, and every step then compares the candidate slots. Up to four steps:
-// the exact search's window (wider for long rows, so that more first counts
-// land in it); more steps, or no cap: the 2k window, whose steps compare
-// fewer slots (measured at 1,048,576 x 1,024, k = 64, 8 steps, with the
-// earlier compaction scheme: 832 us with 2 slots against 910 with 8). A
-// search with no cap and eps = 0 never reaches this: its result is the
-// canonical exact top-k, and launch_select runs the exact kernel for it.
+// step, and every step then compares the candidate slots. Up to four steps,
+// and rows of 4,096 columns or more: the exact search's window (wider for
+// long rows, so that more first counts land in it); more steps on shorter
+// rows, or no cap: the 2k window, whose steps compare fewer slots. Measured
+// (one box, us, 2k window against the exact one): 1,048,576 x 1,024 N(0,1),
+// k = 64, 8 steps 829.5 / 826.1; 262,144 x 1,024, k = 32, 6 steps 189.0 /
+// 193.1; 16,384 rows of N(0,1) rounded to steps of 0.25 (ties), 6 steps,
+// k = 64: 2,048 columns 29.0 / 30.0, 4,096 columns 63.5 / 54.7, 8,192
+// columns 222.9 / 138.3; 8,192 columns, k = 32, 5 steps 253.1 / 130.8;
+// 65,536 x 8,192 N(0,1), k = 64, 6 steps 501.8 / 514.4. A search with no
+// cap and eps = 0 never reaches this: its result is the canonical exact
+// top-k, and launch_select runs the exact kernel for it.
 inline int capped_candidate_slots(int q, int k, int max_iter) {
-  if (max_iter >= 0 && max_iter <= 4) return exact_candidate_slots(q, k);
+  if ((max_iter >= 0 && max_iter <= 4) || q >= 64) return exact_candidate_slots(q, k);
   return candidate_slots(q, k);
 }
 
