@@ -132,16 +132,16 @@ void exact_model(SelectArgs& a, int qc) {
   last = Model{a.m, a.k, qc, a.z_first, a.half_step, a.z_first_c, a.half_step_c, a.inv_m};
 }
 
-// Exact search on rows longer than kGroupMinLength: one row per block of
-// four waves (rtopk_group.hpp), on a persistent grid of what fits on the
-// device at once.
-hipError_t launch_group(const SelectArgs& a, int qc, hipStream_t stream) {
+// Exact or capped search on rows longer than kGroupMinLength: one row per
+// block of four waves (rtopk_group.hpp), on a persistent grid of what fits
+// on the device at once.
+hipError_t launch_group(const SelectArgs& a, int qc, bool capped, hipStream_t stream) {
   constexpr int kPerSlot = kWave * kWavesPerRowGroup;
   const int per_wave = (a.m + kPerSlot - 1) / kPerSlot;
   const int q = per_wave <= 24 ? 24 : 32;
   const bool full = a.m == q * kPerSlot;
-  const RowsKernel fn = q == 24 ? group_kernel<24>(full, false, qc)
-                                : group_kernel<32>(full, false, qc);
+  const RowsKernel fn = q == 24 ? group_kernel<24>(full, false, qc, capped)
+                                : group_kernel<32>(full, false, qc, capped);
   if (fn == nullptr) return hipErrorInvalidValue;
   int device = 0;
   hipError_t err = hipGetDevice(&device);
@@ -171,8 +171,12 @@ hipError_t launch_select(const SelectArgs& args, Mode mode, bool u8_index,
   const int qc = mode == Mode::kCapped ? capped_candidate_slots(q, a.k, a.max_iter)
                                        : exact_candidate_slots(q, a.k);
   if (mode != Mode::kCapped || qc > 0) exact_model(a, qc);
-  if (mode == Mode::kExact && a.m > kGroupMinLength && !u8_index)
-    return launch_group(a, qc, stream);
+  // Row groups: exact search above 4,096 columns; capped search above
+  // 6,144 (at 6,000 columns one wave per row was faster: 76.6 against
+  // 101.6 us for 16,384 rows with few distinct values, k = 64, 4 steps).
+  if (!u8_index && ((mode == Mode::kExact && a.m > kGroupMinLength) ||
+                    (mode == Mode::kCapped && a.m > kCappedGroupMinLength)))
+    return launch_group(a, qc, mode == Mode::kCapped, stream);
   const RowsKernel fn = kernel_for(a.m, mode, u8_index, qc);
   if (fn == nullptr) return hipErrorInvalidValue;
   int device = 0;

@@ -2,9 +2,10 @@
 
 // Row-wise top-k for long rows: one row per group of four waves (one block).
 //
-// Method: the exact search of rtopk_rows.hpp (RTop-K summary page,
-// "Approach": a threshold search over the row's values, then the k survivors
-// in column order), with the row spread over the four waves of a block.
+// Method: the exact search and the capped search of rtopk_rows.hpp (RTop-K
+// summary page, "Approach": a threshold search over the row's values, then
+// the k survivors in column order), with the row spread over the four waves
+// of a block.
 //
 // Why: a row of 8,192 floats held by one wave takes 128 registers per lane,
 // so each SIMD runs one such wave and a CU has four rows in flight, each
@@ -101,6 +102,16 @@ __device__ __forceinline__ int row_count(Group& G, const float (&v)[Q], float t)
 __device__ __forceinline__ float row_sum(Group& G, float x) {
   uint32_t all[kG];
   G.exchange1(__float_as_uint(wave_sum(x)), all);
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kG; ++i) s += __uint_as_float(all[i]);
+  return s;
+}
+
+// Sum over the waves of values already reduced within each wave.
+__device__ __forceinline__ float row_sum_of_waves(Group& G, float wave_total) {
+  uint32_t all[kG];
+  G.exchange1(__float_as_uint(wave_total), all);
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < kG; ++i) s += __uint_as_float(all[i]);
@@ -455,9 +466,174 @@ __device__ __forceinline__ void row_exact(Group& G, const float (&vin)[Q],
   row_search<Q, QC>(G, v, k, t, c, h, col0, areas, out, out0);
 }
 
+// The row's output assembled in LDS by all four waves (the candidate areas,
+// free once every wave is past the exchange that follows its last read of
+// them): put() writes a survivor's value bits at entry `rank` and its
+// column at entry ke + rank; lanes not selected, and ranks past k (more
+// than k elements tied at the row maximum), write a spare entry of their
+// own, k + 64 g + lane. flush() then stores the k entries with coalesced
+// stores, each wave a quarter of them, after a barrier.
+struct GroupStaged {
+  uint32_t* area;
+  uint32_t ke;     // entries per array: k + 64 * kG
+  uint32_t spare;  // this lane's spare entry
+
+  __device__ __forceinline__ GroupStaged(uint32_t* a, int k, int g, int lane)
+      : area(a),
+        ke(static_cast<uint32_t>(k + kWave * kG)),
+        spare(static_cast<uint32_t>(k + kWave * g + lane)) {}
+
+  __device__ __forceinline__ void put(uint64_t msk, uint32_t rank, float x, int col) const {
+    const uint32_t pos = min(lane_select(msk, rank, spare), spare);
+    area[pos] = __float_as_uint(x);
+    area[ke + pos] = static_cast<uint32_t>(col);
+  }
+
+  template <typename Out>
+  __device__ __forceinline__ void flush(const Group& G, const Out& out, int k) const {
+    __syncthreads();
+#pragma unroll 1
+    for (int base = G.g * kWave; base < k; base += kG * kWave) {
+      const uint32_t i = static_cast<uint32_t>(base + G.lane);
+      out.store_entry(i, area[i], area[ke + i]);
+    }
+  }
+};
+
+// One specified step of the capped search over the row (capped_step, with
+// a row-wide count): false once the search has stopped. Every wave holds the
+// same bracket, so all of them count (and reach the exchange) alike.
+template <bool EPS0, int Q>
+__device__ __forceinline__ bool row_capped_step(Group& G, const float (&v)[Q],
+                                                CappedState& b, const SelectArgs& a) {
+  if (!(b.steps < static_cast<uint32_t>(a.max_iter))) return false;
+  if constexpr (!EPS0) {
+    if (ballot(b.hi - b.lo > a.eps) == 0) return false;
+  }
+  const float mid = 0.5f * b.lo + 0.5f * b.hi;
+  if ((ballot(b.lo < mid) & ballot(mid < b.hi)) == 0) return false;
+  const int c = row_count(G, v, mid);
+  ++b.steps;
+  b.lo = c >= a.k ? mid : b.lo;
+  b.hi = c <= a.k ? mid : b.hi;
+  return true;
+}
+
+// The capped search (capped_row) on a row held by the group. The row's
+// minimum, maximum and sum of squares are combined across the waves; the
+// elements at or above the exact search's first threshold t0 are staged;
+// when their count lands in the window every wave runs the specified steps
+// on the row's candidate list (each midpoint at or above t0 gets the row's
+// count, each below it takes the c > k branch as the row's count would),
+// then the tie fill: over the candidates when lo >= t0 (wave 0 stores),
+// else over the row. When the first count misses the window the steps count
+// over the whole row.
+template <int Q, bool FULL, int QC, typename Out, typename Out0>
+__device__ __forceinline__ void row_capped(Group& G, const float (&vin)[Q],
+                                           const SelectArgs& a, int m_local, int col0,
+                                           uint32_t* __restrict__ areas,
+                                           const Out& out, const Out0& out0) {
+  const int k = a.k;
+  const int lane = G.lane;
+  float v[Q];
+  float s2 = 0.0f;  // tail positions were read as 0
+#pragma unroll
+  for (int s = 0; s < Q; ++s) {
+    v[s] = vin[s];
+    if constexpr (QC > 0) s2 = fmaf(vin[s], vin[s], s2);
+  }
+  mask_tail<Q, FULL>(m_local, lane, v);
+  float mn = kInf, mx = -kInf;
+#pragma unroll
+  for (int s = 0; s < Q; ++s) {
+    // Tail positions hold -inf (inputs are finite): out of the minimum.
+    mn = fminf(mn, FULL || v[s] > -kInf ? v[s] : kInf);
+    mx = fmaxf(mx, v[s]);
+  }
+  wave_reduce3<OpMin, OpMax, OpAdd>(mn, mx, s2);
+  {
+    uint32_t mns[kG], mxs[kG];
+    G.exchange2(__float_as_uint(mn), __float_as_uint(mx), mns, mxs);
+    mn = kInf;
+    mx = -kInf;
+#pragma unroll
+    for (int i = 0; i < kG; ++i) {
+      mn = fminf(mn, __uint_as_float(mns[i]));
+      mx = fmaxf(mx, __uint_as_float(mxs[i]));
+    }
+  }
+  const bool eps0 = a.eps == 0.0f;
+  auto col = [lane, col0](int s) { return col0 + s * kWave + lane; };
+  CappedState b{mn, mx, a.m, -1, 0u};
+  if constexpr (QC > 0) {
+    constexpr int kW = kWave * QC;
+    s2 = row_sum_of_waves(G, s2);
+    const float r = fminf(__builtin_amdgcn_sqrtf(s2), 1.0e35f);
+    const float t0 = r * a.z_first;
+    const int c0 = row_count_and_stage<Q, QC>(G, v, t0, col0, areas + G.g * 2 * sub_entries<QC>());
+    if (c0 > k && c0 <= kW) {
+      float cv[QC];
+      int ci[QC];
+      row_read_candidates<QC>(G, areas, c0, cv, ci);
+      if (eps0) capped_run<true>(cv, b, a); else capped_run<false>(cv, b, a);
+      if (ballot(b.lo >= t0) != 0) {
+        // Every element >= lo is a candidate; straight stores from wave 0
+        // (the candidate areas may still be read by the other waves).
+        capped_emit<false>(cv, [&ci](int s) { return ci[s]; }, b, k, out0, out0, lane);
+        return;
+      }
+      // lo < t0: A = {x >= hi} lies among the candidates (hi is the row
+      // maximum or a midpoint whose count was at most k, both >= t0). When
+      // wave 0's columns hold B's quota (the first k - |A| elements of
+      // {lo <= x < hi}), wave 0 alone emits: the split fill of capped_row
+      // over its slots, then the rest of A from the candidates. Otherwise
+      // the fill runs over the whole row. (Also testing whether [lo, t0)
+      // is empty, so that B too is among the candidates, cost more than it
+      // saved: 5-6% slower at k = 32 to 128 on rows with few distinct
+      // values.)
+      const int nA = count_ge(cv, b.hi);
+      if (nA >= k) {
+        capped_emit<false>(cv, [&ci](int s) { return ci[s]; }, b, k, out0, out0, lane);
+        return;
+      }
+      uint32_t met_flag = 0;
+      if (G.g == 0) {
+        int nb = 0;
+#pragma unroll
+        for (int s = 0; s < Q; ++s)
+          nb += popc(ballot(v[s] >= b.lo) & ~ballot(v[s] >= b.hi));
+        met_flag = nb >= k - nA ? 1u : 0u;
+      }
+      uint32_t met[kG];
+      G.exchange1(met_flag, met);
+      if (met[0] != 0) {
+        if (G.g == 0) emit_fill_split(v, cv, ci, lane, b.lo, b.hi, k, nA, out);
+      } else {
+        // Straight from each slot, every wave would store each 128-byte
+        // output line in parts.
+        const GroupStaged staged(areas, k, G.g, lane);
+        row_emit_fill(G, v, col, b.lo, b.hi, k, staged);
+        staged.flush(G, out, k);
+      }
+      return;
+    }
+  }
+#pragma unroll 1
+  while (eps0 ? row_capped_step<true>(G, v, b, a) : row_capped_step<false>(G, v, b, a)) {
+  }
+  if constexpr (QC > 0) {
+    // The candidate areas hold k + 256 entries per array (64 QC >= 2k).
+    const GroupStaged staged(areas, k, G.g, lane);
+    row_emit_fill(G, v, col, b.lo, b.hi, k, staged);
+    staged.flush(G, out, k);
+  } else {
+    row_emit_fill(G, v, col, b.lo, b.hi, k, out);
+  }
+}
+
 // The kernel: block b takes rows b, b + gridDim.x, ... (a persistent grid);
 // wave g of the block holds its quarter of each.
-template <int Q, bool FULL, int QC, typename IdxT>
+template <int Q, bool FULL, int QC, bool CAPPED, typename IdxT>
 __global__ __launch_bounds__(kWave * kG) void rows_in_group(SelectArgs a) {
   constexpr int kE = sub_entries<QC>();
   __shared__ uint32_t areas[kG * 2 * kE];
@@ -490,33 +666,41 @@ __global__ __launch_bounds__(kWave * kG) void rows_in_group(SelectArgs a) {
     const OutRow<IdxT, Mode::kExact> out0(a.out_val + r * a.k,
                                           static_cast<IdxT*>(a.out_idx) + r * a.k,
                                           G.g == 0 ? a.k : 0, nullptr, 0u, 0);
-    row_exact<Q, FULL, QC>(G, v, a, m_local, col0, areas, out, out0);
+    if constexpr (CAPPED)
+      row_capped<Q, FULL, QC>(G, v, a, m_local, col0, areas, out, out0);
+    else
+      row_exact<Q, FULL, QC>(G, v, a, m_local, col0, areas, out, out0);
     // The next row's candidates may be written while a slow wave still
     // reads this row's.
     __syncthreads();
   }
 }
 
-template <int Q, bool FULL, typename IdxT>
+template <int Q, bool FULL, bool CAPPED, typename IdxT>
 RowsKernel group_kernel_qc(int qc) {
   switch (qc) {
-    case 1: return rows_in_group<Q, FULL, 1, IdxT>;
-    case 2: return rows_in_group<Q, FULL, 2, IdxT>;
-    case 4: return rows_in_group<Q, FULL, 4, IdxT>;
-    case 8: return rows_in_group<Q, FULL, 8, IdxT>;
-    default: return rows_in_group<Q, FULL, 0, IdxT>;
+    case 1: return rows_in_group<Q, FULL, 1, CAPPED, IdxT>;
+    case 2: return rows_in_group<Q, FULL, 2, CAPPED, IdxT>;
+    case 4: return rows_in_group<Q, FULL, 4, CAPPED, IdxT>;
+    case 8: return rows_in_group<Q, FULL, 8, CAPPED, IdxT>;
+    default: return rows_in_group<Q, FULL, 0, CAPPED, IdxT>;
   }
 }
 
 }  // namespace group_detail
 
-// The exact kernel for rows of up to 4*64*Q columns held by a group of four
-// waves, Q slots per lane per wave. full: the row length is exactly 4*64*Q.
+// The exact (or capped) kernel for rows of up to 4*64*Q columns held by a
+// group of four waves, Q slots per lane per wave. full: the row length is
+// exactly 4*64*Q.
 template <int Q>
-RowsKernel group_kernel(bool full, bool u8_index, int qc) {
+RowsKernel group_kernel(bool full, bool u8_index, int qc, bool capped) {
   using group_detail::group_kernel_qc;
   if (u8_index) return nullptr;
-  return full ? group_kernel_qc<Q, true, int32_t>(qc) : group_kernel_qc<Q, false, int32_t>(qc);
+  if (capped)
+    return full ? group_kernel_qc<Q, true, true, int32_t>(qc)
+                : group_kernel_qc<Q, false, true, int32_t>(qc);
+  return full ? group_kernel_qc<Q, true, false, int32_t>(qc)
+              : group_kernel_qc<Q, false, false, int32_t>(qc);
 }
 
 }  // namespace rtopk

@@ -21,9 +21,11 @@ constexpr int kBlock = kWave * kWavesPerBlock;
 constexpr int row_waves(int q) { return q <= 8 ? 1 : 4; }
 
 // Waves that share one row in the row-group kernel (rtopk_group.hpp), used
-// by the exact search for rows longer than kGroupMinLength.
+// by the exact search for rows longer than kGroupMinLength and by the
+// capped search for rows longer than kCappedGroupMinLength.
 constexpr int kWavesPerRowGroup = 4;
-constexpr int kGroupMinLength = 4096;
+constexpr int kGroupMinLength = 4096;        // exact search: longer rows
+constexpr int kCappedGroupMinLength = 6144;  // capped search: longer rows
 
 // kMaxk: the exact search, plus the dense [n, m] MaxK output (SelectArgs::dense).
 // kBucket: the exact search on buckets: each kernel row is one bucket of an
@@ -86,9 +88,10 @@ template <int Q>
 RowsKernel rows_kernel(bool full, Mode mode, bool u8_index, int qc);
 
 // Defined in rtopk_group.hpp, instantiated in rtopk_group.hip: the exact
-// kernel for rows held by a group of four waves, q slots per lane per wave.
+// (or capped) kernel for rows held by a group of four waves, q slots per lane
+// per wave.
 template <int Q>
-RowsKernel group_kernel(bool full, bool u8_index, int qc);
+RowsKernel group_kernel(bool full, bool u8_index, int qc, bool capped);
 
 // Candidate slots QC the exact search compacts into for q slots and k
 // survivors: the smallest of 1, 2, 4, 8 with 64*QC >= 2k and 2*QC <= q, or 0

@@ -248,6 +248,26 @@ def test_random_long_rows():
         check(x, k, "capped", int(rng.integers(-1, 10)), 0.0, label=f"long{t}")
 
 
+# The capped search on rows held by four waves (more than 6,144 columns):
+# ragged and full lengths, every branch of its tie fill (candidates only,
+# wave 0's split fill, the staged fill over the row, and the full-row steps
+# when the first count misses its window: shifted rows), with and without
+# eps, and row counts above the resident grid.
+@pytest.mark.parametrize("m", [6145, 7000, 8191, 8192])
+def test_capped_long_rows_in_groups(m):
+    rng = np.random.default_rng(900 + m)
+    n = 3000 if m == 8192 else 700
+    fams = {
+        "normal": rng.standard_normal((n, m)).astype(np.float32),
+        "ties": (np.round(rng.standard_normal((n, m)) * 4) / 4).astype(np.float32) + np.float32(0),
+        "shifted": (rng.standard_normal((n, m)) * 3 + 50).astype(np.float32),
+    }
+    for name, x in fams.items():
+        for k in (1, 32, 200):
+            for it, eps in ((1, 0.0), (2, 0.0), (5, 0.0), (12, 0.0), (-1, 1e-3)):
+                check(x, k, "capped", it, eps, label=f"group capped {name} M={m}")
+
+
 def test_outputs_untouched_outside_bounds_and_deterministic():
     n, m, k = 777, 300, 40
     x = torch.from_numpy(workloads.normal(n, m, seed=5)).to(dev())
