@@ -109,10 +109,50 @@ __device__ __forceinline__ void accumulate(const SpgemmArgs& a, int64_t e0,
   const int k = a.k;
   // Idle lanes (lane_edge < 0) address the step's first edge and add nothing.
   const int addr_edge = lane_edge < 0 ? 0 : lane_edge;
-  // Steps whose feature loads are issued together. Four keeps the kernel
-  // at 53 VGPRs and 8 waves per SIMD (measured on the 262,144-node graph:
-  // 582 us against 626 us with eight steps at 5 waves per SIMD).
+  // Steps whose feature loads are issued together (measured on the
+  // 262,144-node graph, without the pipelining below: four steps 582 us at
+  // 8 waves per SIMD, eight 626 us at 5).
   constexpr int U = 4;
+  // One survivor per lane (k <= 64): the next U steps' feature loads are
+  // issued before the current ones are added, so each wave keeps loads in
+  // flight while it works on the LDS accumulators (569 -> 561 us; two or
+  // three steps per batch measured the same).
+  if (k <= kWave) {
+    struct Step {
+      float xv[U], w[U];
+      int xc[U];
+      bool ok[U];
+    };
+    auto load = [&](int64_t b0, Step& st) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t e = b0 + static_cast<int64_t>(u) * P + addr_edge;
+        const int64_t ec = e < s1 ? e : s1 - 1;  // stays inside the staged range
+        const int col = ecol[ec - e0];
+        st.w[u] = eval[ec - e0];
+        const bool live = lane_edge >= 0 && e < s1 &&
+                          static_cast<uint64_t>(static_cast<int64_t>(col)) <
+                              static_cast<uint64_t>(a.n_src);
+        const int64_t j = live ? col : 0;
+        st.xv[u] = a.sp_data[j * k + lane_t];
+        st.xc[u] = static_cast<int>(sidx[j * k + lane_t]);
+        st.ok[u] = live;
+      }
+    };
+    Step cur, nxt;
+    if (s0 < s1) load(s0, cur);
+    for (int64_t b0 = s0; b0 < s1; b0 += static_cast<int64_t>(U) * P) {
+      const int64_t b1 = b0 + static_cast<int64_t>(U) * P;
+      if (b1 < s1) load(b1, nxt);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (cur.ok[u] && static_cast<uint32_t>(cur.xc[u]) < static_cast<uint32_t>(a.m))
+          accp[cur.xc[u]] = fmaf(cur.w[u], cur.xv[u], accp[cur.xc[u]]);
+      }
+      cur = nxt;
+    }
+    return;
+  }
   for (int64_t b0 = s0; b0 < s1; b0 += static_cast<int64_t>(U) * P) {
     for (int t0 = lane_t; t0 < k; t0 += kWave) {
       float xv[U], w[U];
