@@ -65,8 +65,16 @@ CONFIGS = {
 
 def kernel_family(kernel: str) -> str:
     """Family of a kernel name fragment from op_kernel(): the register-resident
-    row kernels are told apart by their mode argument."""
-    return "rows_in_registers" if kernel.startswith("(rtopk::Mode)") else kernel
+    row kernels are told apart by their mode argument; a fragment of several
+    parts ("a&b") belongs to the family of its first part."""
+    first = kernel.split("&")[0]
+    return "rows_in_registers" if first.startswith("(rtopk::Mode)") else first
+
+
+def kernel_matches(kernel: str, name: str) -> bool:
+    """Whether a kernel name from a counter file matches an op_kernel()
+    fragment (every part of "a&b" must occur in it)."""
+    return all(part in name for part in kernel.split("&"))
 
 
 def kernel_source_hash(kernel: str | None = None) -> str:
@@ -107,7 +115,7 @@ def _counter_means(csv_path: str, counter: str, kernel: str):
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            if kernel in name:
+            if kernel_matches(kernel, name):
                 sel.append(float(r["Counter_Value"]))
             elif "neg" in name.lower():
                 ref.append(float(r["Counter_Value"]))
@@ -190,17 +198,22 @@ def op_kernel(args) -> str:
     if args.op == "maxk_forward":
         if args.m <= 1024:
             return "(rtopk::Mode)2"
-        return "rows_in_group" if args.m > 4096 else "(rtopk::Mode)1"
-    # Selection: no cap and eps = 0 is the exact selection.
+        return "rows_in_group&, false, int>" if args.m > 4096 else "(rtopk::Mode)1"
+    # Selection: no cap and eps = 0 is the exact selection. Row groups are
+    # told apart by their CAPPED argument (the last before the index type):
+    # a capped run also launches the exact selection once, for its quality
+    # figures.
     exact = args.mode == "exact" or (getattr(args, "max_iter", 0) < 0
                                      and getattr(args, "eps", 1.0) == 0.0)
     if not exact:
+        if args.m > 6144 and index != "u8":
+            return "rows_in_group&, true, int>"
         return "(rtopk::Mode)0"
     short = _short_kernel(args.m, args.k)
     if short:
         return short
     if args.m > 4096 and index != "u8":
-        return "rows_in_group"
+        return "rows_in_group&, false, int>"
     return "(rtopk::Mode)1"
 
 

@@ -24,11 +24,13 @@
 // one barrier per combination. Every wave therefore computes the same
 // thresholds and takes the same branches, and reaches the same barriers.
 // Candidates (elements above a threshold, when their count fits the window)
-// are written by each wave to an LDS area of its own and read back by every
-// wave as one list in column order; the search on them runs in every wave
-// alike, and only wave 0 stores what it emits. Emissions over the whole row
-// write each wave's own columns at ranks offset by the survivors of the
-// waves before it.
+// are written by each wave to an LDS area of its own and read back as one
+// list in column order. The exact search on them needs no exchange and
+// runs in wave 0 alone; the capped search runs its steps in every wave
+// alike (the branch after them may need the whole group). Emissions from
+// the candidates are wave 0's, assembled in an LDS output area and stored
+// coalesced. Emissions over the whole row write each wave's own columns at
+// ranks offset by the survivors of the waves before it.
 
 #include "rtopk_rows.hpp"
 
@@ -334,13 +336,40 @@ __device__ __forceinline__ void row_read_candidates(const Group& G,
   }
 }
 
+// Entries per array of wave 0's LDS output area: k + 64 (k <= 32 QC, as
+// the window holds at least 2k candidates).
+template <int QC>
+constexpr int out_entries() {
+  return QC > 0 ? 32 * QC + kWave : 1;
+}
+
+// The exact search on the row's candidates (exact_candidates) by wave 0
+// alone: it needs no exchange, so the other waves have nothing left to do
+// for the row. Wave 0 assembles the output row in its LDS output area and
+// stores it with coalesced stores (straight from several candidate slots,
+// each output line would be written in parts).
+template <int QC, typename Out>
+__device__ __forceinline__ void row_candidates_exact(const Group& G,
+                                                     const uint32_t* __restrict__ areas,
+                                                     uint32_t* __restrict__ ostage, int c,
+                                                     int k, float t, float h,
+                                                     const Out& out) {
+  if (G.g != 0) return;
+  float cv[QC];
+  int ci[QC];
+  row_read_candidates<QC>(G, areas, c, cv, ci);
+  const StagedOut<out_entries<QC>(), true> staged(ostage, k, G.lane);
+  exact_candidates<QC>(cv, ci, k, t, c, h, staged);
+  staged.flush(out, k, G.lane);
+}
+
 // Full-row Newton steps when the first count missed the window
 // (exact_row_search, row-wide).
-template <int Q, int QC, typename Out, typename Out0>
+template <int Q, int QC, typename Out>
 __device__ __forceinline__ void row_search(Group& G, const float (&v)[Q], int k,
                                            float t, int c, float h, int col0,
                                            uint32_t* __restrict__ areas,
-                                           const Out& out, const Out0& out0) {
+                                           const Out& out, uint32_t* __restrict__ ostage) {
   constexpr int kW = kWave * QC;
   const int target2 = QC > 0 ? k + kW : 2 * k + 1;
   const float h2 = 2.0f * h;
@@ -369,10 +398,7 @@ __device__ __forceinline__ void row_search(Group& G, const float (&v)[Q], int k,
     }
     if constexpr (QC > 0) {
       if (c > k && c <= kW) {
-        float cv[QC];
-        int ci[QC];
-        row_read_candidates<QC>(G, areas, c, cv, ci);
-        exact_candidates<QC>(cv, ci, k, t, c, h, out0);
+        row_candidates_exact<QC>(G, areas, ostage, c, k, t, h, out);
         return;
       }
     }
@@ -380,11 +406,11 @@ __device__ __forceinline__ void row_search(Group& G, const float (&v)[Q], int k,
   row_settle(G, v, col, k, lo, clo, hi, chi, out);
 }
 
-template <int Q, bool FULL, int QC, typename Out, typename Out0>
+template <int Q, bool FULL, int QC, typename Out>
 __device__ __forceinline__ void row_exact(Group& G, const float (&vin)[Q],
                                           const SelectArgs& a, int m_local, int col0,
                                           uint32_t* __restrict__ areas,
-                                          const Out& out, const Out0& out0) {
+                                          const Out& out, uint32_t* __restrict__ ostage) {
   const int k = a.k;
   const int lane = G.lane;
   float v[Q];
@@ -406,10 +432,7 @@ __device__ __forceinline__ void row_exact(Group& G, const float (&vin)[Q],
   if constexpr (QC > 0) {
     c = row_count_and_stage<Q, QC>(G, v, t, col0, mine);
     if (static_cast<uint32_t>(c - k - 1) < static_cast<uint32_t>(kWave * QC - k)) {
-      float cv[QC];
-      int ci[QC];
-      row_read_candidates<QC>(G, areas, c, cv, ci);
-      exact_candidates<QC>(cv, ci, k, t, c, h, out0);
+      row_candidates_exact<QC>(G, areas, ostage, c, k, t, h, out);
       return;
     }
   } else {
@@ -443,10 +466,7 @@ __device__ __forceinline__ void row_exact(Group& G, const float (&vin)[Q],
       if constexpr (QC > 0) {
         c1 = row_count_and_stage<Q, QC>(G, v, t1, col0, mine);
         if (static_cast<uint32_t>(c1 - k - 1) < static_cast<uint32_t>(kWave * QC - k)) {
-          float cv[QC];
-          int ci[QC];
-          row_read_candidates<QC>(G, areas, c1, cv, ci);
-          exact_candidates<QC>(cv, ci, k, t1, c1, h1, out0);
+          row_candidates_exact<QC>(G, areas, ostage, c1, k, t1, h1, out);
           return;
         }
       } else {
@@ -458,12 +478,12 @@ __device__ __forceinline__ void row_exact(Group& G, const float (&vin)[Q],
       }
       const int mid2 = QC > 0 ? k + kWave * QC : 2 * k + 1;
       if (abs(2 * c1 - mid2) < abs(2 * c - mid2)) {
-        row_search<Q, QC>(G, v, k, t1, c1, h1, col0, areas, out, out0);
+        row_search<Q, QC>(G, v, k, t1, c1, h1, col0, areas, out, ostage);
         return;
       }
     }
   }
-  row_search<Q, QC>(G, v, k, t, c, h, col0, areas, out, out0);
+  row_search<Q, QC>(G, v, k, t, c, h, col0, areas, out, ostage);
 }
 
 // The row's output assembled in LDS by all four waves (the candidate areas,
@@ -528,11 +548,11 @@ __device__ __forceinline__ bool row_capped_step(Group& G, const float (&v)[Q],
 // then the tie fill: over the candidates when lo >= t0 (wave 0 stores),
 // else over the row. When the first count misses the window the steps count
 // over the whole row.
-template <int Q, bool FULL, int QC, typename Out, typename Out0>
+template <int Q, bool FULL, int QC, typename Out>
 __device__ __forceinline__ void row_capped(Group& G, const float (&vin)[Q],
                                            const SelectArgs& a, int m_local, int col0,
                                            uint32_t* __restrict__ areas,
-                                           const Out& out, const Out0& out0) {
+                                           const Out& out, uint32_t* __restrict__ ostage) {
   const int k = a.k;
   const int lane = G.lane;
   float v[Q];
@@ -576,10 +596,14 @@ __device__ __forceinline__ void row_capped(Group& G, const float (&vin)[Q],
       int ci[QC];
       row_read_candidates<QC>(G, areas, c0, cv, ci);
       if (eps0) capped_run<true>(cv, b, a); else capped_run<false>(cv, b, a);
+      auto cand_col = [&ci](int s) { return ci[s]; };
       if (ballot(b.lo >= t0) != 0) {
-        // Every element >= lo is a candidate; straight stores from wave 0
-        // (the candidate areas may still be read by the other waves).
-        capped_emit<false>(cv, [&ci](int s) { return ci[s]; }, b, k, out0, out0, lane);
+        // Every element >= lo is a candidate: wave 0 alone fills from them,
+        // assembling the output row in its LDS output area.
+        if (G.g == 0) {
+          const StagedOut<out_entries<QC>(), true> staged(ostage, k, lane);
+          capped_emit<true>(cv, cand_col, b, k, out, staged, lane);
+        }
         return;
       }
       // lo < t0: A = {x >= hi} lies among the candidates (hi is the row
@@ -593,7 +617,10 @@ __device__ __forceinline__ void row_capped(Group& G, const float (&vin)[Q],
       // values.)
       const int nA = count_ge(cv, b.hi);
       if (nA >= k) {
-        capped_emit<false>(cv, [&ci](int s) { return ci[s]; }, b, k, out0, out0, lane);
+        if (G.g == 0) {
+          const StagedOut<out_entries<QC>(), true> staged(ostage, k, lane);
+          capped_emit<true>(cv, cand_col, b, k, out, staged, lane);
+        }
         return;
       }
       uint32_t met_flag = 0;
@@ -607,7 +634,11 @@ __device__ __forceinline__ void row_capped(Group& G, const float (&vin)[Q],
       uint32_t met[kG];
       G.exchange1(met_flag, met);
       if (met[0] != 0) {
-        if (G.g == 0) emit_fill_split(v, cv, ci, lane, b.lo, b.hi, k, nA, out);
+        if (G.g == 0) {
+          const StagedOut<out_entries<QC>(), true> staged(ostage, k, lane);
+          emit_fill_split(v, cv, ci, lane, b.lo, b.hi, k, nA, staged);
+          staged.flush(out, k, lane);
+        }
       } else {
         // Straight from each slot, every wave would store each 128-byte
         // output line in parts.
@@ -638,6 +669,8 @@ __global__ __launch_bounds__(kWave * kG) void rows_in_group(SelectArgs a) {
   constexpr int kE = sub_entries<QC>();
   __shared__ uint32_t areas[kG * 2 * kE];
   __shared__ uint32_t xch[4 * kG + 2 * kWave];
+  // Wave 0's area to assemble output rows emitted from the candidates.
+  __shared__ uint32_t ostage[2 * out_entries<QC>()];
   Group G;
   G.lane = static_cast<int>(threadIdx.x) & (kWave - 1);
   G.g = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
@@ -661,15 +694,10 @@ __global__ __launch_bounds__(kWave * kG) void rows_in_group(SelectArgs a) {
     const OutRow<IdxT, Mode::kExact> out(a.out_val + r * a.k,
                                          static_cast<IdxT*>(a.out_idx) + r * a.k, a.k,
                                          nullptr, 0u, 0);
-    // Emissions from the shared candidates: wave 0 stores, the others write
-    // to an output of no entries (every store dropped).
-    const OutRow<IdxT, Mode::kExact> out0(a.out_val + r * a.k,
-                                          static_cast<IdxT*>(a.out_idx) + r * a.k,
-                                          G.g == 0 ? a.k : 0, nullptr, 0u, 0);
     if constexpr (CAPPED)
-      row_capped<Q, FULL, QC>(G, v, a, m_local, col0, areas, out, out0);
+      row_capped<Q, FULL, QC>(G, v, a, m_local, col0, areas, out, ostage);
     else
-      row_exact<Q, FULL, QC>(G, v, a, m_local, col0, areas, out, out0);
+      row_exact<Q, FULL, QC>(G, v, a, m_local, col0, areas, out, ostage);
     // The next row's candidates may be written while a slow wave still
     // reads this row's.
     __syncthreads();

@@ -89,10 +89,12 @@ def test_missing_records_are_an_error(tmp_path):
     ("select", "exact", 128, 16, 1, "u8", "bucket_pairs"),
     ("select", "exact", 128, 32, 1, "u8", "(rtopk::Mode)1"),
     ("select", "exact", 126, 16, 1, "u8", "(rtopk::Mode)1"),
-    ("select", "exact", 8192, 64, 1, "i32", "rows_in_group"),
+    ("select", "exact", 8192, 64, 1, "i32", "rows_in_group&, false, int>"),
+    ("select", "capped", 8192, 64, 1, "i32", "rows_in_group&, true, int>"),
+    ("select", "capped", 6000, 64, 1, "i32", "(rtopk::Mode)0"),
     ("select", "exact", 4096, 64, 1, "i32", "(rtopk::Mode)1"),
     ("maxk_forward", "exact", 256, 32, 1, "u8", "(rtopk::Mode)2"),
-    ("maxk_forward", "exact", 8192, 32, 1, "i32", "rows_in_group"),
+    ("maxk_forward", "exact", 8192, 32, 1, "i32", "rows_in_group&, false, int>"),
     ("maxk_backward", "exact", 256, 32, 1, "u8", "scatter_rows"),
     ("bucketed", "exact", 256, 32, 8, "u8", "bucket_lanes"),
     ("bucketed", "exact", 256, 32, 4, "u8", "bucket_lanes"),
@@ -146,6 +148,17 @@ def test_named_configs_and_overrides(monkeypatch):
     assert "src_rows=32768" in bench.workload_name(a)
     monkeypatch.setattr(sys, "argv", ["bench.py", "--op", "spgemm"])
     assert "src_rows" not in bench.workload_name(bench.parse())
+
+
+def test_group_fragments_tell_exact_from_capped():
+    exact = "void rtopk::group_detail::rows_in_group<32, true, 4, false, int>(rtopk::SelectArgs)"
+    capped = "void rtopk::group_detail::rows_in_group<32, true, 4, true, int>(rtopk::SelectArgs)"
+    assert bench.kernel_matches("rows_in_group&, true, int>", capped)
+    assert not bench.kernel_matches("rows_in_group&, true, int>", exact)
+    assert bench.kernel_matches("rows_in_group&, false, int>", exact)
+    assert bench.kernel_family("rows_in_group&, true, int>") == "rows_in_group"
+    assert bench.kernel_source_hash("rows_in_group&, true, int>") == \
+        bench.kernel_source_hash("rows_in_group")
 
 
 def test_source_hash_is_per_kernel():
