@@ -547,14 +547,15 @@ __device__ __forceinline__ bool row_capped_step(Group& G, const float (&v)[Q],
 // when their count lands in the window every wave runs the specified steps
 // on the row's candidate list (each midpoint at or above t0 gets the row's
 // count, each below it takes the c > k branch as the row's count would),
-// then the tie fill: over the candidates when lo >= t0 (wave 0 stores),
-// else over the row. When the first count misses the window the steps count
-// over the whole row.
+// then the tie fill: over the candidates when lo >= t0 (wave 0 stores);
+// else wave 0's split fill when its columns hold B's quota; else over the
+// row, assembled in the candidate areas. When the first count misses the
+// window the steps count over the whole row.
 template <int Q, bool FULL, int QC, typename Out>
 __device__ __forceinline__ void row_capped(Group& G, const float (&vin)[Q],
                                            const SelectArgs& a, int m_local, int col0,
                                            uint32_t* __restrict__ areas,
-                                           const Out& out, uint32_t* __restrict__ ostage) {
+                                           const Out& out) {
   const int k = a.k;
   const int lane = G.lane;
   float v[Q];
@@ -686,7 +687,7 @@ __global__ __launch_bounds__(kWave * kG) void rows_in_group(SelectArgs a) {
                                          static_cast<IdxT*>(a.out_idx) + r * a.k, a.k,
                                          nullptr, 0u, 0);
     if constexpr (CAPPED)
-      row_capped<Q, FULL, QC>(G, v, a, m_local, col0, areas, out, ostage);
+      row_capped<Q, FULL, QC>(G, v, a, m_local, col0, areas, out);
     else
       row_exact<Q, FULL, QC>(G, v, a, m_local, col0, areas, out, ostage);
     // The next row's candidates may be written while a slow wave still
