@@ -373,53 +373,97 @@ __device__ __forceinline__ float wave_sum(float a) {
   return lane63(a);
 }
 
-// N wave-wide sums interleaved (each DPP step of one hides the
-// read-after-write wait of the others): the same steps, in the same order,
-// as wave_sum on each.
-template <int N>
-__device__ __forceinline__ void wave_sum_n(float (&a)[N]) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) a[i] += dpp<kQuadSwap1>(a[i]);
-#pragma unroll
-  for (int i = 0; i < N; ++i) a[i] += dpp<kQuadSwap2>(a[i]);
-#pragma unroll
-  for (int i = 0; i < N; ++i) a[i] += dpp<kRowHalfMirror>(a[i]);
-#pragma unroll
-  for (int i = 0; i < N; ++i) a[i] += dpp<kRowMirror>(a[i]);
-#pragma unroll
-  for (int i = 0; i < N; ++i) a[i] += dpp<kRowBcast15>(a[i]);
-#pragma unroll
-  for (int i = 0; i < N; ++i) a[i] += dpp<kRowBcast31>(a[i]);
-#pragma unroll
-  for (int i = 0; i < N; ++i) a[i] = lane63(a[i]);
+// Wave-wide reductions of a group's values, four at a time (N a multiple
+// of four, all results uniform). gfx950's lane swaps fold two values per
+// instruction pair: permlane32_swap(a, b) leaves a's lanes 0-31 and b's
+// lanes 0-31 in one register, a's lanes 32-63 and b's lanes 32-63 in the
+// other, so one op reduces a to 32 lanes (0-31) and b to 32 lanes (32-63);
+// permlane16_swap then does the same for 16-lane rows, leaving four values
+// reduced to one 16-lane row each (value 0 in row 0, 2 in row 1, 1 in row 2,
+// 3 in row 3). Four in-row DPP steps finish all four at once. Per four
+// values: 3 swaps, 7 ops and 4 reads of a lane, against 28 instructions as
+// four separate reductions. The sums come out in another order than
+// wave_sum's; min and max are exact in any order.
+template <class Op>
+__device__ __forceinline__ float fold_pair32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b),
+                                                  false, false);
+  return Op::f(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// N triples of wave-wide reductions (minimum, maximum, sum) interleaved;
-// the same steps, in the same order, as wave_reduce3 on each triple.
+template <class Op>
+__device__ __forceinline__ float fold_pair16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b),
+                                                  false, false);
+  return Op::f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// The reductions of N values (N % 4 == 0) with one op, in steps, so that
+// the steps of several of them can be interleaved (each hides the waits of
+// the others).
+template <class Op, int N>
+struct GroupReduce {
+  static_assert(N % 4 == 0, "groups of four values");
+  static constexpr int G = N / 4;
+  float (&a)[N];
+  float f[2 * G];
+
+  // 64 -> 32 lanes, then 32 -> 16 lanes.
+  __device__ __forceinline__ void fold32() {
+#pragma unroll
+    for (int g = 0; g < 2 * G; ++g) f[g] = fold_pair32<Op>(a[2 * g], a[2 * g + 1]);
+  }
+  __device__ __forceinline__ void fold16() {
+#pragma unroll
+    for (int g = 0; g < G; ++g) f[g] = fold_pair16<Op>(f[2 * g], f[2 * g + 1]);
+  }
+  template <int C>
+  __device__ __forceinline__ void in_row() {
+#pragma unroll
+    for (int g = 0; g < G; ++g) f[g] = Op::f(f[g], dpp<C>(f[g]));
+  }
+  __device__ __forceinline__ void finish() {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      a[4 * g] = lane_value(f[g], 0);
+      a[4 * g + 1] = lane_value(f[g], 32);
+      a[4 * g + 2] = lane_value(f[g], 16);
+      a[4 * g + 3] = lane_value(f[g], 48);
+    }
+  }
+};
+
+template <class... R>
+__device__ __forceinline__ void run_group_reduce(R&... r) {
+  (r.fold32(), ...);
+  (r.fold16(), ...);
+  (r.template in_row<kQuadSwap1>(), ...);
+  (r.template in_row<kQuadSwap2>(), ...);
+  (r.template in_row<kRowHalfMirror>(), ...);
+  (r.template in_row<kRowMirror>(), ...);
+  (r.finish(), ...);
+}
+
+// N wave-wide sums (N % 4 == 0).
+template <int N>
+__device__ __forceinline__ void wave_sum_n(float (&a)[N]) {
+  GroupReduce<OpAdd, N> s{a};
+  run_group_reduce(s);
+}
+
+// N triples of wave-wide reductions (minimum, maximum, sum; N % 4 == 0).
 template <int N>
 __device__ __forceinline__ void wave_minmaxsum_n(float (&mn)[N], float (&mx)[N],
                                                  float (&sm)[N]) {
-  auto step = [&](auto ctrl) {
-    constexpr int C = decltype(ctrl)::value;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      mn[i] = fminf(mn[i], dpp<C>(mn[i]));
-      mx[i] = fmaxf(mx[i], dpp<C>(mx[i]));
-      sm[i] = sm[i] + dpp<C>(sm[i]);
-    }
-  };
-  step(std::integral_constant<int, kQuadSwap1>{});
-  step(std::integral_constant<int, kQuadSwap2>{});
-  step(std::integral_constant<int, kRowHalfMirror>{});
-  step(std::integral_constant<int, kRowMirror>{});
-  step(std::integral_constant<int, kRowBcast15>{});
-  step(std::integral_constant<int, kRowBcast31>{});
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    mn[i] = lane63(mn[i]);
-    mx[i] = lane63(mx[i]);
-    sm[i] = lane63(sm[i]);
-  }
+  GroupReduce<OpMin, N> a{mn};
+  GroupReduce<OpMax, N> b{mx};
+  GroupReduce<OpAdd, N> c{sm};
+  run_group_reduce(a, b, c);
 }
 
 // The float right after f in the order of order_key.
@@ -1189,9 +1233,11 @@ __global__ __launch_bounds__(kWave * row_waves(Q)) void rows_in_registers(Select
     // of squares; the capped search's minima, maxima and sums of squares):
     // one chain of dependent DPP steps instead of one per row (262,144 x
     // 256, 4 rows per group: exact 56.0 -> 53.9 us, capped with 2 steps
-    // 59.6 -> 57.3 us). Groups of two rows (512 to 1,024 columns) keep them
-    // inside the search (0.6% faster at 1,024 columns), as does the capped
-    // search without candidates.
+    // 59.6 -> 57.3 us), and with the lane swaps of wave_reduce_groups,
+    // half the instructions of separate reductions (capped with 2 steps
+    // 56.9 -> 55.0 us, 4 steps 59.3 -> 57.2 us). Groups of two rows (512 to
+    // 1,024 columns) keep them inside the search (0.6% faster at 1,024
+    // columns), as does the capped search without candidates.
     constexpr bool kGiven = D >= 4 && (MODE != Mode::kCapped || QC > 0);
     float s2g[D], mng[D], mxg[D];
     if constexpr (kGiven) {
