@@ -601,7 +601,7 @@ constexpr bool stage_whole_row() {
 }
 
 // Entries of the staging area that ranks can reach; 64 spare entries (one
-// per lane) follow them.
+// per bank) follow them.
 template <int Q, int QC>
 constexpr int stage_reach() {
   return stage_whole_row<Q>() ? kWave * Q : kWave * QC;
@@ -618,19 +618,25 @@ constexpr int stage_entries() {
 // E + e, E = stage_entries (two separate words, so no register pairing).
 // The staging is only used when the count lands in (k, 64*QC]. Every lane
 // writes (no exec-mask changes): lanes whose element is below t, and ranks
-// past the reachable part, write the lane's spare entry (never read).
+// past the reachable part, write the last spare entry (never read), all at
+// that one address. Writes of several lanes to one address do not conflict,
+// and a slot's candidates take consecutive entries, so a write meets a bank
+// conflict only when its candidates' run reaches that entry's bank (with a
+// spare entry per lane, 44% of the kernel's LDS cycles were conflicts; a
+// spare entry moved per slot to the bank just below the run removes them
+// all but costs more instructions than it saves).
 template <int Q, int QC>
 __device__ __forceinline__ int count_and_stage(const float (&v)[Q], float t,
                                                int lane,
                                                uint32_t* __restrict__ scratch) {
   constexpr uint32_t kE = stage_entries<Q, QC>();
-  const uint32_t spare = stage_reach<Q, QC>() + static_cast<uint32_t>(lane);
+  constexpr uint32_t kSpare = stage_reach<Q, QC>() + kWave - 1;
   uint32_t base = 0;
 #pragma unroll
   for (int s = 0; s < Q; ++s) {
     const uint64_t msk = ballot(v[s] >= t);
-    uint32_t e = lane_select(msk, rank_below(msk, base), spare);
-    if constexpr (!stage_whole_row<Q>()) e = min(e, spare);
+    uint32_t e = lane_select(msk, rank_below(msk, base), kSpare);
+    if constexpr (!stage_whole_row<Q>()) e = min(e, kSpare);
     scratch[e] = __float_as_uint(v[s]);
     scratch[kE + e] = static_cast<uint32_t>(s * kWave + lane);
     base += popc(msk);
@@ -714,17 +720,17 @@ __device__ __forceinline__ void wave_reduce3(float& a, float& b, float& c) {
 // and flush() stores each array of the row with one coalesced store per 64
 // entries. Straight to memory, an emission over several slots writes each
 // 128-byte output line in parts, one store per slot. Lanes not selected
-// write the lane's spare entry k + lane; entries past k are never stored.
-// Ranks past k arise only when more than k elements tie at the row maximum:
-// with CLAMP (the area does not hold a whole row) they are clamped to the
-// spare entry.
+// all write one spare entry, k + 63 (as in count_and_stage); entries past
+// k are never stored. Ranks past k arise only when more than k elements tie
+// at the row maximum: with CLAMP (the area does not hold a whole row) they
+// are clamped to the spare entry.
 template <int KE, bool CLAMP>
 struct StagedOut {
   uint32_t* area;
   uint32_t spare;
 
-  __device__ __forceinline__ StagedOut(uint32_t* a, int k, int lane)
-      : area(a), spare(static_cast<uint32_t>(k + lane)) {}
+  __device__ __forceinline__ StagedOut(uint32_t* a, int k, int /*lane*/)
+      : area(a), spare(static_cast<uint32_t>(k + kWave - 1)) {}
 
   __device__ __forceinline__ void put(uint64_t msk, uint32_t rank, float x,
                                       int col) const {
