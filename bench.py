@@ -40,7 +40,7 @@ FAMILY_SOURCES = {
     "rows_in_registers": ["rtopk_rows.hpp"],
     "rows_in_group": ["rtopk_rows.hpp", "rtopk_group.hpp"],
     "bucket_lanes": ["rtopk_bucket.hip"],
-    "bucket_pairs": ["rtopk_bucket.hip"],
+    "bucket_quads": ["rtopk_bucket.hip"],
     "scatter_rows": ["rtopk_maxk.hip"],
     "spgemm_rows": ["rtopk_spgemm.hip"],
     "sspmm_rows": ["rtopk_spgemm.hip"],
@@ -179,7 +179,7 @@ def _short_kernel(width: int, kb: int):
     if width <= 64 and kb <= 8:
         return "bucket_lanes"
     if width <= 128 and kb <= 16 and width % 4 == 0:
-        return "bucket_pairs"
+        return "bucket_quads"
     return None
 
 

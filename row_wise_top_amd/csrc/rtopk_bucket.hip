@@ -14,7 +14,7 @@
 // every element above the kb-th largest value and the first few equal to
 // it. A wave takes 64 consecutive buckets, so its loads and stores cover
 // one contiguous stretch of the input and of the outputs. Buckets of 65 to
-// 128 columns keeping at most 16 take two lanes each (bucket_pairs below).
+// 128 columns keeping at most 16 take four lanes each (bucket_quads below).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -437,52 +437,65 @@ __device__ __forceinline__ void merge_top_desc(float (&t)[N], const float (&u)[N
 }
 
 // Buckets of 65 to 128 columns keeping at most 16 (w a multiple of 4, x
-// 16-byte aligned): two lanes per bucket, lane l taking bucket l mod 32 of
-// a group of 32 and its half l / 32 (columns [64h, 64h + 64)). Each lane
-// finds the KB largest values of its half (median-of-three insertion, or
-// sorted batches for 16); the two sorted lists are exchanged between lanes
-// l and l ^ 32 and merged (merge_top_desc), so both lanes hold the
-// bucket's KB largest values. Each lane then
-// keeps its places at or above the kb-th of them; surplus ties at that
-// value are dropped from the highest columns (the low half keeps its equal
-// places first). The low half emits its survivors first, the high half
-// after them, so the bucket's entries are in column order. Persistent grid
-// and staging as in bucket_lanes: the next group's loads are in flight
-// while the current group is selected.
-constexpr int kPairWidth = kPairBucketWidth;  // bucket capacity (two halves of 64)
-constexpr int kPairGroup = kWave / 2;  // buckets per group
+// 16-byte aligned): four lanes per bucket, lane l taking bucket l mod 16 of
+// a group of 16 and its quarter h = l / 16 (columns [32h, 32h + 32)). Each
+// lane finds the KB largest values of its quarter (median-of-three
+// insertion, or two sorted batches of 16 merged); the sorted lists are
+// merged with the lane l ^ 16 (the other quarter of the same half), then
+// with lane l ^ 32 (merge_top_desc), so all four lanes hold the bucket's KB
+// largest values. Each lane then keeps its places at or above the kb-th of
+// them; surplus ties at that value are dropped from the highest columns
+// (lower quarters keep their equal places first). Each quarter emits its
+// survivors after those of the quarters before it, so the bucket's entries
+// are in column order. Persistent grid and staging as in bucket_lanes: the
+// next group's loads are in flight while the current group is selected.
+//
+// The layout is set by occupancy. With two lanes per bucket (32 buckets, a
+// 17 KB stage and 64 places per lane) the kernel held 235 registers and ran
+// two waves per SIMD, its vector unit idle half the time (waiting on LDS
+// and permutes); four lanes per bucket halve the stage (16 buckets, 8.4 KB)
+// and the registers, for four waves per SIMD, at the cost of a second
+// cross-lane merge.
+constexpr int kQuadWidth = kQuadBucketWidth;   // bucket capacity
+constexpr int kQuadGroup = kWave / 4;          // buckets per group
+constexpr int kQuarter = kQuadWidth / 4;       // places per lane
 
 template <int KB, typename IdxT>
-__global__ __launch_bounds__(kWave) void bucket_pairs(SelectArgs a) {
-  constexpr int kHalf = kPairWidth / 2;
-  constexpr int kStride = kPairWidth + 4;  // LDS floats per bucket
-  constexpr int kChunks = kPairWidth / 4;  // 16-byte chunks per bucket
-  constexpr int kLoads = kPairGroup * kChunks / kWave;  // chunks per lane
-  __shared__ u32x4 stage[kPairGroup * kStride / 4];
+__global__ __launch_bounds__(kWave) void bucket_quads(SelectArgs a) {
+  constexpr int kStride = kQuadWidth + 4;  // LDS floats per bucket (skew of 16 bytes)
+  constexpr int kChunks = kQuadWidth / 4;  // 16-byte chunks per bucket
+  constexpr int kLoads = kQuadGroup * kChunks / kWave;  // chunks per lane
+  static_assert(kWave / kChunks == 2, "a load covers two buckets");
+  __shared__ u32x4 stage[kQuadGroup * kStride / 4];
   const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
-  const int bl = lane & (kPairGroup - 1);  // bucket within the group
-  const int h = lane / kPairGroup;         // half
-  const int partner = (lane ^ kPairGroup) << 2;  // ds_bpermute address
+  const int bl = lane & (kQuadGroup - 1);  // bucket within the group
+  const int h = lane / kQuadGroup;         // quarter
+  const int across = (lane ^ kQuadGroup) << 2;       // ds_bpermute: quarter h ^ 1
+  const int other = (lane ^ (2 * kQuadGroup)) << 2;  // quarter h ^ 2
   const int w = a.m, kb = a.k;
-  const int64_t groups = (a.n + kPairGroup - 1) / kPairGroup;
+  const int64_t groups = (a.n + kQuadGroup - 1) / kQuadGroup;
   int64_t grp = blockIdx.x;
   if (grp >= groups) return;
   auto live_of = [&](int64_t g) {
-    const int64_t rest = a.n - g * kPairGroup;
-    return rest < kPairGroup ? static_cast<int>(rest) : kPairGroup;
+    const int64_t rest = a.n - g * kQuadGroup;
+    return rest < kQuadGroup ? static_cast<int>(rest) : kQuadGroup;
   };
-  // Chunk c = 64 i + lane (16 bytes) is place 4 (c mod 32) of bucket c / 32
-  // of the group; chunks past the group's buckets read zeros and chunks
-  // past a bucket (w < 128) belong to the next one: neither is written to
-  // LDS below.
+  // Load i covers buckets 2i and 2i + 1 (lane / 32 picks the bucket, lane
+  // mod 32 the chunk) through a resource of its own that starts at bucket
+  // 2i and ends at the group's end: every load takes the same lane offset,
+  // and the bounds check drops chunks past the group's buckets (they read
+  // zeros). Chunks past a bucket's end (w < 128) belong to the next bucket
+  // and are not written to LDS below.
+  const int load_off = ((lane / kChunks) * w + 4 * (lane % kChunks)) * 4;
   auto load = [&](int64_t g, u32x4 (&q)[kLoads]) {
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(a.x + g * kPairGroup * w), 0, live_of(g) * w * 4, kRsrcWord3);
+    const float* x0 = a.x + g * kQuadGroup * w;
+    const int bytes = live_of(g) * w * 4;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int c = i * kWave + lane;
-      q[i] = __builtin_amdgcn_raw_buffer_load_b128(
-          rx, ((c / kChunks) * w + 4 * (c % kChunks)) * 4, 0, kLoadPolicy);
+      const int skip = i * 8 * w;
+      const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(x0) + 2 * i * w, 0, bytes > skip ? bytes - skip : 0, kRsrcWord3);
+      q[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, load_off, 0, kLoadPolicy);
     }
   };
   u32x4 q[kLoads];
@@ -491,20 +504,36 @@ __global__ __launch_bounds__(kWave) void bucket_pairs(SelectArgs a) {
   // (the staging below writes places < w only), which takes them out of
   // every comparison (the inputs are finite). Written after the first
   // loads are issued, so that they do not wait behind it.
-  if (w < kPairWidth) {
+  if (w < kQuadWidth) {
     constexpr u32x4 kNegInf = {0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u};
-    for (int i = lane; i < kPairGroup * kStride / 4; i += kWave) stage[i] = kNegInf;
+    for (int i = lane; i < kQuadGroup * kStride / 4; i += kWave) stage[i] = kNegInf;
   }
+  // Load i lands at stage chunk i * (2 * kStride / 4) + (lane / 32) *
+  // kStride / 4 + lane mod 32: each half-wave writes 512 consecutive bytes.
+  const int stage_at = (lane / kChunks) * (kStride / 4) + (lane % kChunks);
+  // Sums over the bucket's four quarters of a per-lane count: the count of
+  // the quarters before this lane's, and the bucket's total. The permutes run
+  // on every lane (a permute reading an inactive lane yields 0).
+  auto quarter_prefix = [&](int c, int& before, int& total) {
+    const int c_x = __builtin_amdgcn_ds_bpermute(across, c);
+    const int pair = c + c_x;
+    const int pair_o = __builtin_amdgcn_ds_bpermute(other, pair);
+    before = ((h & 1) ? c_x : 0) + ((h & 2) ? pair_o : 0);
+    total = pair + pair_o;
+  };
   const uint32_t nb = static_cast<uint32_t>(a.buckets);
   for (;;) {
-    const int64_t g0 = grp * kPairGroup;
+    const int64_t g0 = grp * kQuadGroup;
     const int live = live_of(grp);
+    if (w == kQuadWidth && live == kQuadGroup) {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int c = i * kWave + lane;
-      const int bkt = c / kChunks;
-      const int p = 4 * (c % kChunks);
-      if (p < w && bkt < live) stage[(bkt * kStride + p) / 4] = q[i];
+      for (int i = 0; i < kLoads; ++i) stage[i * (2 * kStride / 4) + stage_at] = q[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const int bkt = 2 * i + lane / kChunks;
+        if (4 * (lane % kChunks) < w && bkt < live) stage[i * (2 * kStride / 4) + stage_at] = q[i];
+      }
     }
     // LDS operations of one wave complete in issue order; the barriers keep
     // the compiler from moving the reads above the writes (and, at the
@@ -513,114 +542,98 @@ __global__ __launch_bounds__(kWave) void bucket_pairs(SelectArgs a) {
     asm volatile("" ::: "memory");
     const int64_t next = grp + gridDim.x;
     if (next < groups) load(next, q);
-    const float* row = reinterpret_cast<const float*>(stage) + bl * kStride + kHalf * h;
-    float v[kHalf];
+    // The lane's quarter: 16 lanes of one quarter read 16 buckets whose
+    // rows are 528 bytes apart, so the 16-byte reads fall in 16 different
+    // bank groups.
+    const float* row = reinterpret_cast<const float*>(stage) + bl * kStride + kQuarter * h;
+    float v[kQuarter];
 #pragma unroll
-    for (int j = 0; j < kHalf; j += 4) {
+    for (int j = 0; j < kQuarter; j += 4) {
       const u32x4 e = *reinterpret_cast<const u32x4*>(row + j);
       v[j] = __uint_as_float(e.x);
       v[j + 1] = __uint_as_float(e.y);
       v[j + 2] = __uint_as_float(e.z);
       v[j + 3] = __uint_as_float(e.w);
     }
-    // The KB largest values of the half, largest first. Up to 8: by
-    // median-of-three insertion (KB instructions per place). 16: in sorted
-    // batches of 16 (odd-even merge sort, 63 compare-exchanges) merged into
-    // the list (16 maxima and 32 compare-exchanges), about 13 instructions
-    // per place instead of 16.
+    // The KB largest values of the quarter, largest first. Up to 8: by
+    // median-of-three insertion (KB instructions per place). 16: two sorted
+    // batches of 16 (odd-even merge sort, 63 compare-exchanges each) merged.
     float tv[KB];
     if constexpr (KB >= 16) {
+      float bt[KB];
 #pragma unroll
-      for (int i = 0; i < KB; ++i) tv[i] = v[i];
-      sort_desc(tv);
-#pragma unroll
-      for (int j0 = KB; j0 < kHalf; j0 += KB) {
-        float bt[KB];
-#pragma unroll
-        for (int i = 0; i < KB; ++i) bt[i] = v[j0 + i];
-        sort_desc(bt);
-        merge_top_desc(tv, bt);
+      for (int i = 0; i < KB; ++i) {
+        tv[i] = v[i];
+        bt[i] = v[KB + i];
       }
+      sort_desc(tv);
+      sort_desc(bt);
+      merge_top_desc(tv, bt);
     } else {
 #pragma unroll
       for (int i = 0; i < KB; ++i) tv[i] = -__builtin_inff();
 #pragma unroll
-      for (int j = 0; j < kHalf; ++j) {
+      for (int j = 0; j < kQuarter; ++j) {
         const float x = v[j];
 #pragma unroll
         for (int i = KB - 1; i > 0; --i) tv[i] = __builtin_amdgcn_fmed3f(tv[i - 1], x, tv[i]);
         tv[0] = fmaxf(tv[0], x);
       }
     }
-    // The bucket's KB largest values: this list merged with the other
-    // half's.
-    float cv[KB], ov[KB];
+    // The bucket's KB largest values: merged with the other quarter of the
+    // half, then with the other half.
+    {
+      float ov[KB];
 #pragma unroll
-    for (int i = 0; i < KB; ++i) {
-      cv[i] = tv[i];
-      ov[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(tv[i])));
+      for (int i = 0; i < KB; ++i)
+        ov[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(across, __float_as_int(tv[i])));
+      merge_top_desc(tv, ov);
+#pragma unroll
+      for (int i = 0; i < KB; ++i)
+        ov[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(other, __float_as_int(tv[i])));
+      merge_top_desc(tv, ov);
     }
-    merge_top_desc(cv, ov);
     // The kb-th largest value of the bucket and how many of the kb largest
     // equal it.
-    float thr = cv[0];
+    float thr = tv[0];
 #pragma unroll
-    for (int i = 1; i < KB; ++i) thr = i < kb ? cv[i] : thr;
+    for (int i = 1; i < KB; ++i) thr = i < kb ? tv[i] : thr;
     int need_eq = 0;
 #pragma unroll
-    for (int i = 0; i < KB; ++i) need_eq += (i < kb && cv[i] == thr) ? 1 : 0;
-    // Places of the half at or above thr: place j at bit 31 - (j mod 32)
-    // of word j / 32.
-    uint32_t keep[2];
-    int count = 0;
+    for (int i = 0; i < KB; ++i) need_eq += (i < kb && tv[i] == thr) ? 1 : 0;
+    // Places of the quarter at or above thr: place j at bit 31 - j.
     const float thr_s = zero_as_minus(thr);
+    uint32_t below = 0;
 #pragma unroll
-    for (int qw = 0; qw < 2; ++qw) {
-      uint32_t below = 0;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) below = shift_in_lt(below, v[32 * qw + j], thr_s);
-      keep[qw] = ~below;
-      count += __builtin_popcount(keep[qw]);
-    }
-    const int count_other = __builtin_amdgcn_ds_bpermute(partner, count);
-    if (__builtin_amdgcn_ballot_w64(count + count_other > kb) != 0) {
+    for (int j = 0; j < kQuarter; ++j) below = shift_in_lt(below, v[j], thr_s);
+    uint32_t keep = ~below;
+    int count = __builtin_popcount(keep);
+    int base, total;
+    quarter_prefix(count, base, total);
+    if (__builtin_amdgcn_ballot_w64(total > kb) != 0) {
       // Surplus ties at thr: keep every place above it and the need_eq
-      // lowest-column places equal to it, low half first.
-      uint32_t equal[2];
-      int eq = 0;
+      // lowest-column places equal to it, lower quarters first.
+      uint32_t equal = 0;
 #pragma unroll
-      for (int qw = 0; qw < 2; ++qw) {
-        equal[qw] = 0;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) shift_in_eq(equal[qw], v[32 * qw + j], thr);
-        keep[qw] &= ~equal[qw];
-        eq += __builtin_popcount(equal[qw]);
-      }
-      const int eq_other = __builtin_amdgcn_ds_bpermute(partner, eq);
-      const int quota = h == 0 ? need_eq : need_eq - (eq_other < need_eq ? eq_other : need_eq);
+      for (int j = 0; j < kQuarter; ++j) shift_in_eq(equal, v[j], thr);
+      keep &= ~equal;
+      int eq_before, eq_total;
+      quarter_prefix(__builtin_popcount(equal), eq_before, eq_total);
+      const int quota = need_eq - eq_before;
 #pragma unroll
       for (int i = 0; i < KB; ++i) {
-        bool done = i >= quota;
-#pragma unroll
-        for (int qw = 0; qw < 2; ++qw) {
-          const uint32_t top = equal[qw] != 0u ? 0x80000000u >> __builtin_clz(equal[qw]) : 0u;
-          const bool take = !done && top != 0u;
-          keep[qw] |= take ? top : 0u;
-          equal[qw] ^= take ? top : 0u;
-          done = done || take;
-        }
+        const uint32_t top = equal != 0u ? 0x80000000u >> __builtin_clz(equal) : 0u;
+        const uint32_t take = i < quota ? top : 0u;
+        keep |= take;
+        equal ^= take;
       }
-      count = __builtin_popcount(keep[0]) + __builtin_popcount(keep[1]);
+      count = __builtin_popcount(keep);
+      quarter_prefix(count, base, total);
     }
-    // The high half's entries follow the low half's. The exchange runs on
-    // every lane: a permute evaluated only where h == 1 would read the low
-    // half's lanes while they are inactive, which yields 0.
-    const int count_low = __builtin_amdgcn_ds_bpermute(partner, count);
-    const int base = h == 0 ? 0 : count_low;
     const uint32_t r0 = g0 < 0x100000000LL ? static_cast<uint32_t>(g0) % nb
                                            : static_cast<uint32_t>(g0 % a.buckets);
     const uint32_t first =
-        ((r0 + static_cast<uint32_t>(bl)) % nb) * static_cast<uint32_t>(w) + kHalf * h;
+        ((r0 + static_cast<uint32_t>(bl)) % nb) * static_cast<uint32_t>(w) + kQuarter * h;
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         a.out_val + g0 * kb, 0, live * kb * 4, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc(
@@ -633,17 +646,9 @@ __global__ __launch_bounds__(kWave) void bucket_pairs(SelectArgs a) {
     int cols[KB];
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
-      int col = 0;
-      bool found = false;
-#pragma unroll
-      for (int qw = 0; qw < 2; ++qw) {
-        const bool here = !found && keep[qw] != 0u;
-        const int c = keep[qw] != 0u ? __builtin_clz(keep[qw]) : 0;
-        col = here ? 32 * qw + c : col;
-        keep[qw] &= here ? ~(0x80000000u >> c) : ~0u;
-        found = found || here;
-      }
-      cols[i] = col;
+      const int c = keep != 0u ? __builtin_clz(keep) : 0;
+      cols[i] = c;
+      keep &= ~(0x80000000u >> c);
     }
     uint32_t xs[KB];
 #pragma unroll
@@ -665,10 +670,10 @@ __global__ __launch_bounds__(kWave) void bucket_pairs(SelectArgs a) {
 }
 
 template <typename IdxT>
-RowsKernel pick_pair(int kb) {
-  if (kb <= 4) return bucket_pairs<4, IdxT>;
-  if (kb <= 8) return bucket_pairs<8, IdxT>;
-  return bucket_pairs<16, IdxT>;
+RowsKernel pick_quad(int kb) {
+  if (kb <= 4) return bucket_quads<4, IdxT>;
+  if (kb <= 8) return bucket_quads<8, IdxT>;
+  return bucket_quads<16, IdxT>;
 }
 
 template <int W, bool VEC, typename IdxT>
@@ -696,7 +701,7 @@ RowsKernel pick(int w, int kb, bool vec) {
 
 bool bucket_lanes_supported(const float* x, int width, int kb) {
   if (width <= kLaneBucketWidth) return kb <= kLaneBucketSurvivors;
-  return width <= kPairBucketWidth && kb <= kPairBucketSurvivors && width % 4 == 0 &&
+  return width <= kQuadBucketWidth && kb <= kQuadBucketSurvivors && width % 4 == 0 &&
          (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
 }
 
@@ -704,14 +709,14 @@ hipError_t launch_bucket_lanes(const SelectArgs& a, bool u8_index,
                                hipStream_t stream) {
   using namespace bucket_detail;
   const bool vec = a.m % 4 == 0 && (reinterpret_cast<uintptr_t>(a.x) & 15u) == 0;
-  const bool pairs = a.m > kLaneBucketWidth;
-  if (pairs && (!vec || a.m > kPairWidth || a.k > kPairBucketSurvivors))
+  const bool quads = a.m > kLaneBucketWidth;
+  if (quads && (!vec || a.m > kQuadWidth || a.k > kQuadBucketSurvivors))
     return hipErrorInvalidValue;
-  const RowsKernel fn = pairs ? (u8_index ? pick_pair<uint8_t>(a.k) : pick_pair<int32_t>(a.k))
+  const RowsKernel fn = quads ? (u8_index ? pick_quad<uint8_t>(a.k) : pick_quad<int32_t>(a.k))
                               : (u8_index ? pick<uint8_t>(a.m, a.k, vec)
                                           : pick<int32_t>(a.m, a.k, vec));
   const int threads = kLaneWaves * kWave;
-  const int per_block = pairs ? kPairGroup : threads;
+  const int per_block = quads ? kQuadGroup : threads;
   int64_t blocks = (a.n + per_block - 1) / per_block;
   // Staged groups (16-byte loads, buckets of more than 16 columns): a
   // persistent grid of what is resident; the waves loop over the groups.

@@ -279,20 +279,21 @@ __device__ __forceinline__ void row_settle(Group& G, const float (&v)[Q],
 
 // LDS candidate area of one wave: values at [0, E), columns at [E, 2E),
 // E = kWave * QC + kWave (the candidates of one wave never exceed the row's
-// window; ranks past it go to the lane's spare entry).
+// window; ranks past it go to the spare entry).
 template <int QC>
 constexpr int sub_entries() {
   return kWave * QC + kWave;
 }
 
 // #{x >= t} over the row; each wave also writes its elements >= t, in column
-// order, to its own candidate area (see count_and_stage).
+// order, to its own candidate area (see count_and_stage: the lanes not
+// writing a candidate all write the last entry).
 template <int Q, int QC>
 __device__ __forceinline__ int row_count_and_stage(Group& G, const float (&v)[Q],
                                                    float t, int col0,
                                                    uint32_t* __restrict__ area) {
   constexpr uint32_t kE = sub_entries<QC>();
-  const uint32_t spare = kWave * QC + static_cast<uint32_t>(G.lane);
+  constexpr uint32_t spare = kWave * QC + kWave - 1;
   uint32_t base = 0;
 #pragma unroll
   for (int s = 0; s < Q; ++s) {
@@ -492,18 +493,19 @@ __device__ __forceinline__ void row_exact(Group& G, const float (&vin)[Q],
 // free once every wave is past the exchange that follows its last read of
 // them): put() writes a survivor's value bits at entry `rank` and its
 // column at entry ke + rank; lanes not selected, and ranks past k (more
-// than k elements tied at the row maximum), write a spare entry of their
-// own, k + 64 g + lane. flush() then stores the k entries with coalesced
-// stores, each wave a quarter of them, after a barrier.
+// than k elements tied at the row maximum), write the wave's spare entry,
+// k + 64 g + 63 (one address for all of them, as in count_and_stage).
+// flush() then stores the k entries with coalesced stores, each wave a
+// quarter of them, after a barrier.
 struct GroupStaged {
   uint32_t* area;
   uint32_t ke;     // entries per array: k + 64 * kG
-  uint32_t spare;  // this lane's spare entry
+  uint32_t spare;  // this wave's spare entry
 
-  __device__ __forceinline__ GroupStaged(uint32_t* a, int k, int g, int lane)
+  __device__ __forceinline__ GroupStaged(uint32_t* a, int k, int g, int /*lane*/)
       : area(a),
         ke(static_cast<uint32_t>(k + kWave * kG)),
-        spare(static_cast<uint32_t>(k + kWave * g + lane)) {}
+        spare(static_cast<uint32_t>(k + kWave * g + kWave - 1)) {}
 
   __device__ __forceinline__ void put(uint64_t msk, uint32_t rank, float x, int col) const {
     const uint32_t pos = min(lane_select(msk, rank, spare), spare);

@@ -201,15 +201,15 @@ hipError_t launch_sspmm(SpgemmArgs a, bool u8_index, hipStream_t stream);
 
 // Bucketed top-k with short buckets (rtopk_bucket.hip): one lane per bucket
 // for buckets of at most kLaneBucketWidth columns keeping at most
-// kLaneBucketSurvivors each; two lanes per bucket for buckets of up to
-// kPairBucketWidth columns keeping at most kPairBucketSurvivors, where the
+// kLaneBucketSurvivors each; four lanes per bucket for buckets of up to
+// kQuadBucketWidth columns keeping at most kQuadBucketSurvivors, where the
 // width is a multiple of 4 and x is 16-byte aligned. `a` is the bucket view
 // (n = rows * buckets, m = bucket width, k = survivors per bucket, buckets
 // = buckets per row).
 constexpr int kLaneBucketWidth = 64;
 constexpr int kLaneBucketSurvivors = 8;
-constexpr int kPairBucketWidth = 128;
-constexpr int kPairBucketSurvivors = 16;
+constexpr int kQuadBucketWidth = 128;
+constexpr int kQuadBucketSurvivors = 16;
 bool bucket_lanes_supported(const float* x, int width, int kb);
 hipError_t launch_bucket_lanes(const SelectArgs& a, bool u8_index,
                                hipStream_t stream);

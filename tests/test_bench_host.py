@@ -86,7 +86,7 @@ def test_missing_records_are_an_error(tmp_path):
     ("select", "exact", 256, 32, 1, "u8", "(rtopk::Mode)1"),
     ("select", "capped", 256, 32, 1, "u8", "(rtopk::Mode)0"),
     ("select", "exact", 64, 8, 1, "u8", "bucket_lanes"),
-    ("select", "exact", 128, 16, 1, "u8", "bucket_pairs"),
+    ("select", "exact", 128, 16, 1, "u8", "bucket_quads"),
     ("select", "exact", 128, 32, 1, "u8", "(rtopk::Mode)1"),
     ("select", "exact", 126, 16, 1, "u8", "(rtopk::Mode)1"),
     ("select", "exact", 8192, 64, 1, "i32", "rows_in_group&, false, int>"),
@@ -98,7 +98,7 @@ def test_missing_records_are_an_error(tmp_path):
     ("maxk_backward", "exact", 256, 32, 1, "u8", "scatter_rows"),
     ("bucketed", "exact", 256, 32, 8, "u8", "bucket_lanes"),
     ("bucketed", "exact", 256, 32, 4, "u8", "bucket_lanes"),
-    ("bucketed", "exact", 256, 32, 2, "u8", "bucket_pairs"),
+    ("bucketed", "exact", 256, 32, 2, "u8", "bucket_quads"),
     ("bucketed", "exact", 256, 64, 2, "u8", "(rtopk::Mode)3"),
     ("bucketed", "exact", 512, 32, 2, "i32", "(rtopk::Mode)3"),
     ("spgemm", "exact", 256, 32, 1, "u8", "spgemm_rows"),

@@ -44,8 +44,8 @@ CASES = [  # (n, m, k, buckets)
     (81, 96, 12, 4), (70, 2048, 512, 64), (66, 8192, 256, 256),
     (120, 256, 32, 4), (90, 200, 20, 4), (77, 96, 8, 2), (60, 128, 2, 2),
     (45, 132, 24, 3),
-    # Buckets of 65 to 128 columns keeping at most 16 (two lanes per bucket,
-    # 32 buckets per wave) where the width is a multiple of 4; other widths
+    # Buckets of 65 to 128 columns keeping at most 16 (four lanes per bucket,
+    # 16 buckets per wave) where the width is a multiple of 4; other widths
     # take the wave kernel.
     (257, 256, 32, 2), (300, 200, 10, 2), (130, 272, 24, 4), (99, 340, 20, 4),
     (65, 384, 12, 3), (70, 248, 2, 2), (1000, 256, 16, 2), (31, 256, 30, 2),

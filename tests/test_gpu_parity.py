@@ -321,7 +321,7 @@ def test_nonnull_stream():
 
 
 # Short rows with few survivors take one lane per row (64 rows per wave), or
-# two (32 rows per wave) for 65 to 128 columns keeping at most 16: row
+# four (16 rows per wave) for 65 to 128 columns keeping at most 16: row
 # lengths around the 8/16/32/64/128-column classes, every survivor class,
 # row counts that end inside a wave, tie-heavy and adversarial rows, and an
 # input that starts one float past a 16-byte boundary (4-byte loads; the
