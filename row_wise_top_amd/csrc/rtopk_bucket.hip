@@ -33,6 +33,7 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kLoadPolicy = 0;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // acc = 2 * acc + (x < t), from the sign of x - t: for finite x and t the
 // difference is rounded once, so it is negative exactly when x < t, except
@@ -111,6 +112,48 @@ __device__ __forceinline__ void select_bucket(const SelectArgs& a, int64_t g0, i
     else
       __builtin_amdgcn_raw_buffer_store_b32(first + col, ri, e * 4, 0, 0);
   };
+  // All KB entries of the lane, when kb == KB and both outputs are 16-byte
+  // aligned: the lane's entries are then one contiguous piece of each
+  // output, stored with the widest stores (one 16-byte value store per four
+  // entries), so each store instruction writes whole lines. Entry by entry,
+  // every store instruction wrote 64 scattered words. Lanes past the
+  // group's end store past the resources' end (dropped).
+  const bool vec_out = kb == KB && ((reinterpret_cast<uintptr_t>(a.out_val) |
+                                     reinterpret_cast<uintptr_t>(a.out_idx)) & 15) == 0;
+  auto put_all = [&](const uint32_t (&xb)[KB], const int (&col)[KB]) {
+    if (KB > 1 && vec_out) {
+      if constexpr (KB == 2) {
+        const u32x2 xv = {xb[0], xb[1]};
+        __builtin_amdgcn_raw_buffer_store_b64(xv, rv, lane * 8, 0, 0);
+        if constexpr (sizeof(IdxT) == 1) {
+          const uint32_t iv = ((first + col[0]) & 0xffu) | (((first + col[1]) & 0xffu) << 8);
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(iv), ri, lane * 2, 0, 0);
+        } else {
+          const u32x2 iv = {first + col[0], first + col[1]};
+          __builtin_amdgcn_raw_buffer_store_b64(iv, ri, lane * 8, 0, 0);
+        }
+      } else if constexpr (KB >= 4) {
+#pragma unroll
+        for (int c = 0; c < KB; c += 4) {
+          const u32x4 xv = {xb[c], xb[c + 1], xb[c + 2], xb[c + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(xv, rv, (lane * KB + c) * 4, 0, 0);
+          if constexpr (sizeof(IdxT) == 1) {
+            uint32_t iv = 0;
+#pragma unroll
+            for (int j = 3; j >= 0; --j) iv = (iv << 8) | ((first + col[c + j]) & 0xffu);
+            __builtin_amdgcn_raw_buffer_store_b32(iv, ri, lane * KB + c, 0, 0);
+          } else {
+            const u32x4 iv = {first + col[c], first + col[c + 1], first + col[c + 2],
+                              first + col[c + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(iv, ri, (lane * KB + c) * 4, 0, 0);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KB; ++i) put(i, __uint_as_float(xb[i]), static_cast<uint32_t>(col[i]));
+    }
+  };
   if constexpr (KB <= 2) {
     // The KB best so far with their columns, largest first. Empty places
     // hold -inf (inputs are finite, so the first KB elements always enter).
@@ -153,8 +196,7 @@ __device__ __forceinline__ void select_bucket(const SelectArgs& a, int64_t g0, i
       tb[1] = sw ? b0 : tb[1];
       tc[1] = sw ? c0 : tc[1];
     }
-#pragma unroll
-    for (int i = 0; i < KB; ++i) put(i, __uint_as_float(tb[i]), static_cast<uint32_t>(tc[i]));
+    put_all(tb, tc);
   } else {
     // The KB largest values (a multiset, largest first) by median-of-three
     // insertion: with tv sorted, place i becomes med3(tv[i-1], x, tv[i]).
@@ -238,17 +280,15 @@ __device__ __forceinline__ void select_bucket(const SelectArgs& a, int64_t g0, i
       }
       cols[i] = col;
     }
-    float xs[KB];
+    uint32_t xs[KB];
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
       if constexpr (kStage)
-        xs[i] = row[cols[i]];
+        xs[i] = __float_as_uint(row[cols[i]]);
       else
-        xs[i] = __uint_as_float(
-            __builtin_amdgcn_raw_buffer_load_b32(rx, base + cols[i] * 4, 0, 0));
+        xs[i] = __builtin_amdgcn_raw_buffer_load_b32(rx, base + cols[i] * 4, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < KB; ++i) put(i, xs[i], static_cast<uint32_t>(cols[i]));
+    put_all(xs, cols);
   }
 }
 
@@ -460,13 +500,24 @@ constexpr int kQuadWidth = kQuadBucketWidth;   // bucket capacity
 constexpr int kQuadGroup = kWave / 4;          // buckets per group
 constexpr int kQuarter = kQuadWidth / 4;       // places per lane
 
-template <int KB, typename IdxT>
+// VEC_OUT: both outputs are 16-byte aligned (the outputs are then stored
+// in 16-byte pieces; every group's stretch starts at a multiple of 16 kb
+// entries).
+template <int KB, bool VEC_OUT, typename IdxT>
 __global__ __launch_bounds__(kWave) void bucket_quads(SelectArgs a) {
   constexpr int kStride = kQuadWidth + 4;  // LDS floats per bucket (skew of 16 bytes)
   constexpr int kChunks = kQuadWidth / 4;  // 16-byte chunks per bucket
   constexpr int kLoads = kQuadGroup * kChunks / kWave;  // chunks per lane
   static_assert(kWave / kChunks == 2, "a load covers two buckets");
   __shared__ u32x4 stage[kQuadGroup * kStride / 4];
+  // The output assembly area at the start of the stage: kOutEntries value
+  // words and a spare one, then the indices (bytes or words) from word
+  // kOutIdx, and their spare entry.
+  constexpr int kOutEntries = kQuadGroup * KB;
+  constexpr int kOutIdx = kOutEntries + 4;
+  constexpr int kOutWords = kOutIdx + (sizeof(IdxT) == 1 ? kOutEntries / 4 + 4 : kOutEntries + 4);
+  static_assert(kOutEntries % 64 == 0 || kOutEntries <= 256, "one store per array");
+  static_assert(kOutWords <= kQuadGroup * kStride, "assembly fits the stage");
   const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
   const int bl = lane & (kQuadGroup - 1);  // bucket within the group
   const int h = lane / kQuadGroup;         // quarter
@@ -601,7 +652,18 @@ __global__ __launch_bounds__(kWave) void bucket_quads(SelectArgs a) {
     int need_eq = 0;
 #pragma unroll
     for (int i = 0; i < KB; ++i) need_eq += (i < kb && tv[i] == thr) ? 1 : 0;
-    // Places of the quarter at or above thr: place j at bit 31 - j.
+    // Places of the quarter at or above thr: place j at bit 31 - j. The
+    // quarter is read from the stage again: holding it across the merges
+    // would take 32 more registers (and a wave per SIMD).
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < kQuarter; j += 4) {
+      const u32x4 e = *reinterpret_cast<const u32x4*>(row + j);
+      v[j] = __uint_as_float(e.x);
+      v[j + 1] = __uint_as_float(e.y);
+      v[j + 2] = __uint_as_float(e.z);
+      v[j + 3] = __uint_as_float(e.w);
+    }
     const float thr_s = zero_as_minus(thr);
     uint32_t below = 0;
 #pragma unroll
@@ -639,28 +701,88 @@ __global__ __launch_bounds__(kWave) void bucket_quads(SelectArgs a) {
     const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<IdxT*>(a.out_idx) + g0 * kb, 0,
         live * kb * static_cast<int>(sizeof(IdxT)), kRsrcWord3);
-    // Columns of the lane's survivors, lowest first; then their values (the
-    // LDS reads issued together rather than one wait per survivor); then
-    // the stores. Entries past the lane's survivors store past the
-    // resources' end, where the hardware drops them.
-    int cols[KB];
+    // The values of the lane's survivors, lowest column first (the LDS
+    // reads issued together rather than one wait per survivor).
+    uint32_t xs[KB];
+    {
+      uint32_t k2 = keep;
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        const int c = k2 != 0u ? __builtin_clz(k2) : 0;
+        xs[i] = __float_as_uint(row[c]);
+        k2 &= ~(0x80000000u >> c);
+      }
+    }
+    // The group's outputs are one contiguous stretch of live * kb entries
+    // (at most 1 KB of values): they are assembled in the stage (free once
+    // the reads above are done; LDS operations of one wave complete in
+    // issue order) and stored with one coalesced store per array. Stored
+    // straight from each lane, every entry was a 4-byte (and a 1-byte)
+    // store of its own: 32 store instructions per group, each writing 64
+    // scattered words, which kept the texture address unit busy 70% of the
+    // time. Entries past a lane's survivors write the spare entry; the
+    // columns are found again rather than kept in registers.
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    uint32_t* const out_val = reinterpret_cast<uint32_t*>(stage);
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
       const int c = keep != 0u ? __builtin_clz(keep) : 0;
-      cols[i] = c;
       keep &= ~(0x80000000u >> c);
-    }
-    uint32_t xs[KB];
-#pragma unroll
-    for (int i = 0; i < KB; ++i) xs[i] = __float_as_uint(row[cols[i]]);
-#pragma unroll
-    for (int i = 0; i < KB; ++i) {
-      const int e = i < count ? bl * kb + base + i : (1 << 28);
-      __builtin_amdgcn_raw_buffer_store_b32(xs[i], rv, e * 4, 0, 0);
+      const int e = i < count ? bl * kb + base + i : kOutEntries;
+      out_val[e] = xs[i];
       if constexpr (sizeof(IdxT) == 1)
-        __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(first + cols[i]), ri, e, 0, 0);
+        reinterpret_cast<uint8_t*>(out_val + kOutIdx)[e] = static_cast<uint8_t>(first + c);
       else
-        __builtin_amdgcn_raw_buffer_store_b32(first + cols[i], ri, e * 4, 0, 0);
+        out_val[kOutIdx + e] = first + c;
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    // Lane l stores entries 4l .. 4l + 3 of each array (16-byte value
+    // stores when the output is 16-byte aligned, else four words); the
+    // resources' bounds drop entries past live * kb.
+    {
+      const u32x4 vals = reinterpret_cast<const u32x4*>(out_val)[lane];
+      if constexpr (VEC_OUT) {
+        __builtin_amdgcn_raw_buffer_store_b128(vals, rv, lane * 16, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b32(vals.x, rv, lane * 16, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(vals.y, rv, lane * 16 + 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(vals.z, rv, lane * 16 + 8, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(vals.w, rv, lane * 16 + 12, 0, 0);
+      }
+      if constexpr (sizeof(IdxT) == 1) {
+        const uint32_t idx4 = out_val[kOutIdx + lane];
+        // The bounds check drops a word that is only partly in range: the
+        // lane holding the last entries of a stretch whose length is not a
+        // multiple of 4 stores them byte by byte.
+        const int n_idx = live * kb;
+        if (VEC_OUT && 4 * lane + 4 <= n_idx) {
+          __builtin_amdgcn_raw_buffer_store_b32(idx4, ri, lane * 4, 0, 0);
+        } else {
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(idx4 >> (8 * b)), ri,
+                                                 lane * 4 + b, 0, 0);
+        }
+      } else {
+        const u32x4 idx = reinterpret_cast<const u32x4*>(out_val + kOutIdx)[lane];
+        if constexpr (VEC_OUT) {
+          __builtin_amdgcn_raw_buffer_store_b128(idx, ri, lane * 16, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b32(idx.x, ri, lane * 16, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(idx.y, ri, lane * 16 + 4, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(idx.z, ri, lane * 16 + 8, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(idx.w, ri, lane * 16 + 12, 0, 0);
+        }
+      }
+    }
+    // Short buckets: the assembly overwrote places past w of the first
+    // bucket rows, which must read -inf.
+    if (w < kQuadWidth) {
+      __builtin_amdgcn_wave_barrier();
+      constexpr u32x4 kNegInf = {0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u};
+      for (int i = lane; i < kOutWords / 4; i += kWave) stage[i] = kNegInf;
     }
     if (next >= groups) break;
     grp = next;
@@ -669,11 +791,18 @@ __global__ __launch_bounds__(kWave) void bucket_quads(SelectArgs a) {
   }
 }
 
+template <bool VEC_OUT, typename IdxT>
+RowsKernel pick_quad_kb(int kb) {
+  if (kb <= 4) return bucket_quads<4, VEC_OUT, IdxT>;
+  if (kb <= 8) return bucket_quads<8, VEC_OUT, IdxT>;
+  return bucket_quads<16, VEC_OUT, IdxT>;
+}
+
 template <typename IdxT>
-RowsKernel pick_quad(int kb) {
-  if (kb <= 4) return bucket_quads<4, IdxT>;
-  if (kb <= 8) return bucket_quads<8, IdxT>;
-  return bucket_quads<16, IdxT>;
+RowsKernel pick_quad(const SelectArgs& a) {
+  const bool vec_out = ((reinterpret_cast<uintptr_t>(a.out_val) |
+                         reinterpret_cast<uintptr_t>(a.out_idx)) & 15) == 0;
+  return vec_out ? pick_quad_kb<true, IdxT>(a.k) : pick_quad_kb<false, IdxT>(a.k);
 }
 
 template <int W, bool VEC, typename IdxT>
@@ -712,7 +841,7 @@ hipError_t launch_bucket_lanes(const SelectArgs& a, bool u8_index,
   const bool quads = a.m > kLaneBucketWidth;
   if (quads && (!vec || a.m > kQuadWidth || a.k > kQuadBucketSurvivors))
     return hipErrorInvalidValue;
-  const RowsKernel fn = quads ? (u8_index ? pick_quad<uint8_t>(a.k) : pick_quad<int32_t>(a.k))
+  const RowsKernel fn = quads ? (u8_index ? pick_quad<uint8_t>(a) : pick_quad<int32_t>(a))
                               : (u8_index ? pick<uint8_t>(a.m, a.k, vec)
                                           : pick<int32_t>(a.m, a.k, vec));
   const int threads = kLaneWaves * kWave;

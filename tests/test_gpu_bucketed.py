@@ -107,3 +107,25 @@ def test_bucketed_unaligned_input(m, k, b):
     torch.cuda.synchronize()
     assert_identical((v.cpu().numpy(), i.cpu().numpy().astype(np.int32)),
                      oracle.bucketed(x_np, k, b), f"unaligned m={m} k={k} b={b}")
+
+
+@pytest.mark.parametrize("m,k,b", [(256, 32, 8), (256, 16, 8), (128, 16, 8), (96, 12, 4),
+                                   (256, 32, 2), (256, 30, 2), (200, 20, 2)])
+@pytest.mark.parametrize("u8", [False, True])
+def test_bucketed_unaligned_outputs(m, k, b, u8):
+    # Outputs starting one element past a 16-byte boundary: the short-bucket
+    # kernels then store entry by entry instead of in 16-byte pieces.
+    import row_wise_top_amd as rt
+    n = 203
+    x_np = workloads.normal(n, m, 800 + m + k)
+    x = torch.from_numpy(x_np).to("cuda:0")
+    dt = torch.uint8 if u8 else torch.int32
+    fv = torch.full((n * k + 1,), -1.0, dtype=torch.float32, device="cuda:0")
+    fi = torch.zeros((n * k + 1,), dtype=dt, device="cuda:0")
+    v, i = fv[1:].view(n, k), fi[1:].view(n, k)
+    assert v.data_ptr() % 16 != 0 and i.data_ptr() % 16 != 0
+    rt.rtopk_select_bucketed(x, k, b, out_val=v, out_idx=i, index_dtype=dt)
+    torch.cuda.synchronize()
+    assert fv[0].item() == -1.0 and fi[0].item() == 0
+    assert_identical((v.cpu().numpy(), i.cpu().numpy().astype(np.int32)),
+                     oracle.bucketed(x_np, k, b), f"unaligned outputs m={m} k={k} b={b} u8={u8}")
