@@ -496,6 +496,24 @@ __device__ __forceinline__ void merge_top_desc(float (&t)[N], const float (&u)[N
 // and permutes); four lanes per bucket halve the stage (16 buckets, 8.4 KB)
 // and the registers, for four waves per SIMD, at the cost of a second
 // cross-lane merge.
+// A value of lane l and of its partner l ^ D (D = 16 or 32), through the
+// gfx950 lane swaps: lo receives the value of the lane whose bit D is clear,
+// hi that of the lane whose bit D is set (each lane gets both; swapping x
+// with itself exchanges the two rows, or halves, of the wave).
+template <int D>
+__device__ __forceinline__ void swap_rows(uint32_t x, uint32_t& lo, uint32_t& hi) {
+  static_assert(D == 16 || D == 32, "row or half swaps");
+  if constexpr (D == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    lo = r[0];
+    hi = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    lo = r[0];
+    hi = r[1];
+  }
+}
+
 constexpr int kQuadWidth = kQuadBucketWidth;   // bucket capacity
 constexpr int kQuadGroup = kWave / 4;          // buckets per group
 constexpr int kQuarter = kQuadWidth / 4;       // places per lane
@@ -521,8 +539,6 @@ __global__ __launch_bounds__(kWave) void bucket_quads(SelectArgs a) {
   const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
   const int bl = lane & (kQuadGroup - 1);  // bucket within the group
   const int h = lane / kQuadGroup;         // quarter
-  const int across = (lane ^ kQuadGroup) << 2;       // ds_bpermute: quarter h ^ 1
-  const int other = (lane ^ (2 * kQuadGroup)) << 2;  // quarter h ^ 2
   const int w = a.m, kb = a.k;
   const int64_t groups = (a.n + kQuadGroup - 1) / kQuadGroup;
   int64_t grp = blockIdx.x;
@@ -563,14 +579,16 @@ __global__ __launch_bounds__(kWave) void bucket_quads(SelectArgs a) {
   // kStride / 4 + lane mod 32: each half-wave writes 512 consecutive bytes.
   const int stage_at = (lane / kChunks) * (kStride / 4) + (lane % kChunks);
   // Sums over the bucket's four quarters of a per-lane count: the count of
-  // the quarters before this lane's, and the bucket's total. The permutes run
-  // on every lane (a permute reading an inactive lane yields 0).
+  // the quarters before this lane's, and the bucket's total (see
+  // swap_rows: lo holds the even quarter of each pair, then the first half).
   auto quarter_prefix = [&](int c, int& before, int& total) {
-    const int c_x = __builtin_amdgcn_ds_bpermute(across, c);
-    const int pair = c + c_x;
-    const int pair_o = __builtin_amdgcn_ds_bpermute(other, pair);
-    before = ((h & 1) ? c_x : 0) + ((h & 2) ? pair_o : 0);
-    total = pair + pair_o;
+    uint32_t lo, hi;
+    swap_rows<16>(static_cast<uint32_t>(c), lo, hi);
+    const int pair = static_cast<int>(lo + hi);
+    uint32_t lo2, hi2;
+    swap_rows<32>(static_cast<uint32_t>(pair), lo2, hi2);
+    before = ((h & 1) ? static_cast<int>(lo) : 0) + ((h & 2) ? static_cast<int>(lo2) : 0);
+    total = static_cast<int>(lo2 + hi2);
   };
   const uint32_t nb = static_cast<uint32_t>(a.buckets);
   for (;;) {
@@ -632,17 +650,27 @@ __global__ __launch_bounds__(kWave) void bucket_quads(SelectArgs a) {
       }
     }
     // The bucket's KB largest values: merged with the other quarter of the
-    // half, then with the other half.
+    // half, then with the other half. The lists are exchanged with lane
+    // swaps; each lane of a pair merges the two lists in one orientation or
+    // the other, which yields the same sorted list.
     {
-      float ov[KB];
+      float lo[KB], hi[KB];
 #pragma unroll
-      for (int i = 0; i < KB; ++i)
-        ov[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(across, __float_as_int(tv[i])));
-      merge_top_desc(tv, ov);
+      for (int i = 0; i < KB; ++i) {
+        uint32_t a, b;
+        swap_rows<16>(__float_as_uint(tv[i]), a, b);
+        lo[i] = __uint_as_float(a);
+        hi[i] = __uint_as_float(b);
+      }
+      merge_top_desc(lo, hi);
 #pragma unroll
-      for (int i = 0; i < KB; ++i)
-        ov[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(other, __float_as_int(tv[i])));
-      merge_top_desc(tv, ov);
+      for (int i = 0; i < KB; ++i) {
+        uint32_t a, b;
+        swap_rows<32>(__float_as_uint(lo[i]), a, b);
+        tv[i] = __uint_as_float(a);
+        hi[i] = __uint_as_float(b);
+      }
+      merge_top_desc(tv, hi);
     }
     // The kb-th largest value of the bucket and how many of the kb largest
     // equal it.
