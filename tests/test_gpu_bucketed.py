@@ -50,6 +50,8 @@ CASES = [  # (n, m, k, buckets)
     (257, 256, 32, 2), (300, 200, 10, 2), (130, 272, 24, 4), (99, 340, 20, 4),
     (65, 384, 12, 3), (70, 248, 2, 2), (1000, 256, 16, 2), (31, 256, 30, 2),
     (33, 136, 32, 2), (47, 512, 64, 4),
+    # Buckets of 257 to 384 columns: the wave kernel, groups of four rows.
+    (37, 768, 64, 2), (41, 640, 20, 2), (5, 1152, 60, 3),
 ]
 
 

@@ -367,3 +367,21 @@ def test_short_rows_beyond_resident_grid(n, m, k):
     xq = np.round(x[: n // 2] * 4) / 4 + np.float32(0.0)
     check(np.ascontiguousarray(xq.astype(np.float32)), k, "exact",
           label=f"short ties n={n // 2} M={m}")
+
+
+# Rows of 257 to 384 columns (six slots per lane, groups of four rows per
+# wave): normal rows take the candidate window, shifted and uniform ones the
+# fallback; row counts that end inside a group leave rows of it unused.
+@pytest.mark.parametrize("m", [257, 320, 383, 384])
+def test_six_slot_rows(m):
+    rng = np.random.default_rng(1300 + m)
+    for n in (1, 2, 3, 5, 6, 7, 4099):
+        x = workloads.normal(n, m, seed=1300 + n)
+        for k in (1, 16, 32, 64, m // 2):
+            check(x, k, "exact", label=f"six-slot M={m} n={n} k={k}")
+    x = (rng.standard_normal((777, m)) + 1000.0).astype(np.float32)
+    check(x, 32, "exact", label=f"six-slot shifted M={m}")
+    x = rng.random((777, m)).astype(np.float32)
+    check(x, 24, "exact", label=f"six-slot uniform M={m}")
+    x = workloads.grid_ties(555, m, 5)
+    check(x, 40, "exact", label=f"six-slot ties M={m}")
