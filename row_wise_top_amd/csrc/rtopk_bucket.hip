@@ -297,6 +297,7 @@ __device__ __forceinline__ void select_bucket(const SelectArgs& a, int64_t g0, i
 // waves for 8 and 32 buckets of 256 columns, 7% for 4 buckets).
 constexpr int kLaneWaves = 1;
 constexpr int kSimdsPerCu = 4;
+constexpr int kMaxStagedWavesPerCu = 3 * kSimdsPerCu;
 
 // Staged groups: each wave takes groups blockIdx.x, blockIdx.x + gridDim.x,
 // ... (the host sizes the grid to what is resident, never more than the
@@ -886,6 +887,13 @@ hipError_t launch_bucket_lanes(const SelectArgs& a, bool u8_index,
     if (hipGetDevice(&device) != hipSuccess) return hipErrorInvalidDevice;
     int per_cu = resident_blocks(reinterpret_cast<const void*>(fn), threads, device);
     if (per_cu >= kSimdsPerCu) per_cu -= per_cu % kSimdsPerCu;
+    // At most three waves per SIMD, though 16 fit: each wave keeps a group
+    // (8 KB) of loads in flight, and fewer of them ran faster (one box, us,
+    // 16 -> 12 waves per CU: 262,144 x 256 in 2 buckets 67.4 -> 66.1, in 8
+    // buckets 58.6 -> 57.9; 1,048,576 x 128, k = 16 135.6 -> 131.9, k = 8
+    // 117.9 -> 116.9; 2,097,152 x 32 58.7 -> 57.9; 8 waves: slower on the
+    // four-lane kernel).
+    per_cu = per_cu < kMaxStagedWavesPerCu ? per_cu : kMaxStagedWavesPerCu;
     const int64_t resident = static_cast<int64_t>(cu_count(device)) * per_cu;
     blocks = blocks < resident ? blocks : resident;
   }
