@@ -238,6 +238,8 @@ def parse():
                         "SRC_ROWS rows only (default: all rows). A smaller footprint "
                         "stands for what one XCD would gather from if the edges were "
                         "partitioned by source-row block")
+    p.add_argument("--no-torch-topk", action="store_true",
+                   help="--op select: skip timing torch.topk on the same inputs")
     p.add_argument("--buckets", type=int, default=8,
                    help="buckets per row for --op bucketed")
     p.add_argument("--config", type=int, choices=sorted(CONFIGS), default=None,
@@ -492,6 +494,24 @@ def main():
                 "float_atomics": nnz * k,
                 "kernel_over_reference": avg_launch_ms / ref_ms}
             del g_ref, rows_ref, src_ref
+    if args.op == "select" and not args.no_torch_topk:
+        # Context, not a target: the pages quote their speedups over PyTorch's
+        # topk at M = 256. torch.topk (largest, unsorted, int64 indices) on the
+        # same rotating inputs, timed the same way.
+        for i in range(20):
+            torch.topk(xs[i % nbuf], k, dim=1, largest=True, sorted=False)
+        r0 = torch.cuda.Event(enable_timing=True)
+        r1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        r0.record(stream)
+        for i in range(50):
+            torch.topk(xs[i % nbuf], k, dim=1, largest=True, sorted=False)
+        r1.record(stream)
+        torch.cuda.synchronize()
+        ref_ms = r0.elapsed_time(r1) / 50
+        extra["torch_topk"] = {"what": "torch.topk(x, k, dim=1, sorted=False), same inputs",
+                               "us": ref_ms * 1e3,
+                               "speedup": ref_ms / avg_launch_ms}
     algo_bytes = int(n * per_row)
     achieved = algo_bytes / (avg_launch_ms * 1e-3) / 1e9
     workload = workload_name(args)

@@ -148,6 +148,14 @@ def test_named_configs_and_overrides(monkeypatch):
     assert "src_rows=32768" in bench.workload_name(a)
     monkeypatch.setattr(sys, "argv", ["bench.py", "--op", "spgemm"])
     assert "src_rows" not in bench.workload_name(bench.parse())
+    # The torch.topk context timing is on by default and can be skipped; the
+    # workload name does not depend on it.
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    a = bench.parse()
+    assert not a.no_torch_topk
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--no-torch-topk"])
+    b = bench.parse()
+    assert b.no_torch_topk and bench.workload_name(b) == bench.workload_name(a)
 
 
 def test_group_fragments_tell_exact_from_capped():
