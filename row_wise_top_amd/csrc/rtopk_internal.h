@@ -136,8 +136,14 @@ inline int exact_candidate_slots(int q, int k) {
 // columns 222.9 / 138.3; 8,192 columns, k = 32, 5 steps 253.1 / 130.8;
 // 65,536 x 8,192 N(0,1), k = 64, 6 steps 501.8 / 514.4. A search with no
 // cap and eps = 0 never reaches this: its result is the canonical exact
-// top-k, and launch_select runs the exact kernel for it.
+// top-k, and launch_select runs the exact kernel for it. At most two
+// steps on rows of up to 512 columns: no candidates (the steps and the tie
+// fill count over the row, whose output is assembled in LDS); staging costs
+// more than the two counts it saves (262,144 x 256, k = 32, 2 steps 55.6 ->
+// 54.0 us; 65,536 x 256, k = 32 19.0 -> 18.9 us; with 3 steps staging wins:
+// 57.6 against 58.6 us).
 inline int capped_candidate_slots(int q, int k, int max_iter) {
+  if (max_iter >= 0 && max_iter <= 2 && q <= 8) return 0;
   if ((max_iter >= 0 && max_iter <= 4) || q >= 64) return exact_candidate_slots(q, k);
   return candidate_slots(q, k);
 }

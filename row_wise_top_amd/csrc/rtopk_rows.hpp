@@ -456,6 +456,14 @@ __device__ __forceinline__ void wave_sum_n(float (&a)[N]) {
   run_group_reduce(s);
 }
 
+// N pairs of wave-wide reductions (minimum, maximum; N % 4 == 0).
+template <int N>
+__device__ __forceinline__ void wave_minmax_n(float (&mn)[N], float (&mx)[N]) {
+  GroupReduce<OpMin, N> a{mn};
+  GroupReduce<OpMax, N> b{mx};
+  run_group_reduce(a, b);
+}
+
 // N triples of wave-wide reductions (minimum, maximum, sum; N % 4 == 0).
 template <int N>
 __device__ __forceinline__ void wave_minmaxsum_n(float (&mn)[N], float (&mx)[N],
@@ -940,7 +948,12 @@ __device__ __forceinline__ void capped_row(const float (&vin)[Q], float mn_g,
   constexpr int kKE = QC > 0 ? stage_entries<Q, QC>() : kWave * Q + kWave;
   const StagedOut<kKE, (!stage_whole_row<Q>() && QC > 0)> staged(scratch, k, lane);
   if constexpr (QC == 0) {
-    wave_reduce2<OpMin, OpMax>(mn, mx);
+    if constexpr (GIVEN) {
+      mn = mn_g;
+      mx = mx_g;
+    } else {
+      wave_reduce2<OpMin, OpMax>(mn, mx);
+    }
     CappedState b{mn, mx, a.m, -1, 0u};
     if (eps0) capped_run<true>(v, b, a); else capped_run<false>(v, b, a);
     capped_emit<kStage>(v, row_col, b, k, out, staged, lane);
@@ -1243,8 +1256,8 @@ __global__ __launch_bounds__(kWave * row_waves(Q)) void rows_in_registers(Select
     // half the instructions of separate reductions (capped with 2 steps
     // 56.9 -> 55.0 us, 4 steps 59.3 -> 57.2 us). Groups of two rows (512 to
     // 1,024 columns) keep them inside the search (0.6% faster at 1,024
-    // columns), as does the capped search without candidates.
-    constexpr bool kGiven = D >= 4 && (MODE != Mode::kCapped || QC > 0);
+    // columns).
+    constexpr bool kGiven = D >= 4;
     float s2g[D], mng[D], mxg[D];
     if constexpr (kGiven) {
 #pragma unroll
@@ -1258,7 +1271,11 @@ __global__ __launch_bounds__(kWave * row_waves(Q)) void rows_in_registers(Select
           mask_tail<Q, FULL>(a.m, lane, w);
           lane_min_max<Q, FULL>(w, mng[d], mxg[d]);
         }
-        wave_minmaxsum_n(mng, mxg, s2g);
+        // Without candidates the capped search needs no sum of squares.
+        if constexpr (QC > 0)
+          wave_minmaxsum_n(mng, mxg, s2g);
+        else
+          wave_minmax_n(mng, mxg);
       } else {
         wave_sum_n(s2g);
       }
