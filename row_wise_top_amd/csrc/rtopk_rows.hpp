@@ -919,9 +919,9 @@ __device__ __forceinline__ void lane_min_max(const float (&v)[Q], float& mn, flo
   }
 }
 
-// GIVEN: the caller has reduced the row's minimum, maximum and sum of
-// squares (mn_g, mx_g, s2_g) together with those of its group's other rows
-// (QC > 0 only); otherwise they are computed here.
+// GIVEN: the caller has reduced the row's minimum and maximum (and for
+// QC > 0 its sum of squares) together with those of its group's other rows
+// (mn_g, mx_g, s2_g); otherwise they are computed here.
 template <int Q, bool FULL, int QC, bool GIVEN, typename Out>
 __device__ __forceinline__ void capped_row(const float (&vin)[Q], float mn_g,
                                            float mx_g, float s2_g,
