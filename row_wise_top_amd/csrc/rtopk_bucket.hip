@@ -481,22 +481,23 @@ __device__ __forceinline__ void merge_top_desc(float (&t)[N], const float (&u)[N
 // 16-byte aligned): four lanes per bucket, lane l taking bucket l mod 16 of
 // a group of 16 and its quarter h = l / 16 (columns [32h, 32h + 32)). Each
 // lane finds the KB largest values of its quarter (median-of-three
-// insertion, or two sorted batches of 16 merged); the sorted lists are
-// merged with the lane l ^ 16 (the other quarter of the same half), then
-// with lane l ^ 32 (merge_top_desc), so all four lanes hold the bucket's KB
-// largest values. Each lane then keeps its places at or above the kb-th of
-// them; surplus ties at that value are dropped from the highest columns
-// (lower quarters keep their equal places first). Each quarter emits its
-// survivors after those of the quarters before it, so the bucket's entries
-// are in column order. Persistent grid and staging as in bucket_lanes: the
+// insertion, or two sorted batches of 16 merged); the sorted lists of lanes
+// l and l ^ 16 (the other quarter of the same half), then those of the two
+// halves, are exchanged with lane swaps and merged (merge_top_desc), so all
+// four lanes hold the bucket's KB largest values. Each lane then keeps its
+// places at or above the kb-th of them; surplus ties at that value are
+// dropped from the highest columns (lower quarters keep their equal places
+// first). Each quarter emits its survivors after those of the quarters
+// before it, so the bucket's entries are in column order. Persistent grid and staging as in bucket_lanes: the
 // next group's loads are in flight while the current group is selected.
 //
 // The layout is set by occupancy. With two lanes per bucket (32 buckets, a
 // 17 KB stage and 64 places per lane) the kernel held 235 registers and ran
 // two waves per SIMD, its vector unit idle half the time (waiting on LDS
 // and permutes); four lanes per bucket halve the stage (16 buckets, 8.4 KB)
-// and the registers, for four waves per SIMD, at the cost of a second
-// cross-lane merge.
+// and the registers (up to four waves per SIMD; the host launches three), at
+// the cost of a second cross-lane merge.
+
 // A value of lane l and of its partner l ^ D (D = 16 or 32), through the
 // gfx950 lane swaps: lo receives the value of the lane whose bit D is clear,
 // hi that of the lane whose bit D is set (each lane gets both; swapping x
