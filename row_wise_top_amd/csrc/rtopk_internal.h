@@ -61,13 +61,19 @@ using RowsKernel = void (*)(SelectArgs);
 // Rows a wave of the selection kernel keeps in flight for q slots per lane:
 // the row being worked on plus rows_in_flight(q, dense) - 1 whose loads are
 // issued. About 4 KB of a wave's rows are in flight for rows of at most 384
-// columns; the fused MaxK forward (dense: it also writes each row back
-// whole) keeps two. Short rows (q <= 16) are also the rows each wave takes
-// in all: the grid then covers the matrix once (a wave that loads its rows
-// first and stores last never waits on its own stores, which share the load
-// counter on this GPU). Longer rows get no prefetch and a persistent grid.
+// columns, two rows of 385 to 512; the fused MaxK forward (dense: it also
+// writes each row back whole) keeps two. From 513 columns one row per wave:
+// a second row's search then waited behind the first's (one box, us, two
+// rows -> one: 1,048,576 x 1,024 N(0,1), k = 64 820 -> 771, capped with 4
+// steps 834 -> 765; 16,384 x 1,024 rows with ties, k = 128 21.9 -> 18.5;
+// 262,144 x 768, k = 64 151 -> 144; at 512 columns one row per wave was
+// 6% slower on N(0,1) rows). Short rows (q <= 16) are also the rows each
+// wave takes in all: the grid then covers the matrix once (a wave that
+// loads its rows first and stores last never waits on its own stores,
+// which share the load counter on this GPU). Longer rows get no prefetch
+// and a persistent grid.
 constexpr int rows_in_flight(int q, bool dense) {
-  return q > 16 ? 1 : dense ? 2 : q <= 2 ? 8 : q <= 6 ? 4 : 2;
+  return q > 16 ? 1 : dense ? 2 : q <= 2 ? 8 : q <= 6 ? 4 : q <= 8 ? 2 : 1;
 }
 constexpr bool one_group_per_wave(int q) { return q <= 16; }
 
