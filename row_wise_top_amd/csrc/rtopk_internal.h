@@ -70,12 +70,18 @@ using RowsKernel = void (*)(SelectArgs);
 // 6% slower on N(0,1) rows). Short rows (q <= 16) are also the rows each
 // wave takes in all: the grid then covers the matrix once (a wave that
 // loads its rows first and stores last never waits on its own stores,
-// which share the load counter on this GPU). Longer rows get no prefetch
-// and a persistent grid.
+// which share the load counter on this GPU). Longer rows get no prefetch.
 constexpr int rows_in_flight(int q, bool dense) {
   return q > 16 ? 1 : dense ? 2 : q <= 2 ? 8 : q <= 6 ? 4 : q <= 8 ? 2 : 1;
 }
-constexpr bool one_group_per_wave(int q) { return q <= 16; }
+// Rows of up to 2,048 columns: one group per wave over the whole matrix;
+// the hardware's dispatcher then balances the waves, where a persistent
+// grid's equal shares waited for its slowest waves (one box, us, persistent
+// -> one group per wave: 65,536 x 2,048 N(0,1), k = 64 108.6 -> 92.2;
+// 16,384 x 2,048 tie-heavy rows, k = 32 28.9 -> 26.3, k = 256 32.7 -> 31.0;
+// at 4,096 columns the persistent grid stays ahead, 197.1 against 205.8 on
+// 65,536 N(0,1) rows).
+constexpr bool one_group_per_wave(int q) { return q <= 32; }
 
 // Rows the fused MaxK forward kernel takes (its LDS holds the dense row);
 // longer rows run the selection and then the scatter.
