@@ -168,9 +168,9 @@ def test_adversarial_rows(m):
         check(x, k, "exact", label=f"adv M={m}")
         if m <= 256:
             check(x, k, "exact", u8=True, label=f"adv M={m}")
-        for mi, eps in ((-1, 0.0), (0, 0.0), (1, 0.0), (3, 0.0), (-1, 0.5), (6, 1e-3)):
+        for mi, eps in ((-1, 0.0), (0, 0.0), (1, 0.0), (2, 0.0), (3, 0.0), (-1, 0.5), (6, 1e-3)):
             check(x, k, "capped", mi, eps, label=f"adv M={m}")
-            if m <= 256 and mi in (-1, 3):
+            if m <= 256 and mi in (-1, 2, 3):
                 check(x, k, "capped", mi, eps, u8=True, label=f"adv M={m}")
 
 
@@ -195,6 +195,7 @@ def test_other_value_distributions(dist, m, k):
     x = DISTRIBUTIONS[dist](rng, 1500, m).astype(np.float32) + np.float32(0.0)
     check(x, k, "exact", label=f"{dist} exact")
     check(x, k, "capped", 5, 0.0, label=f"{dist} capped")
+    check(x, k, "capped", 2, 0.0, label=f"{dist} capped two steps")
     if m <= 256:
         check(x, k, "exact", u8=True, label=f"{dist} exact u8")
 
