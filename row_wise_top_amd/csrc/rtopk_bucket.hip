@@ -529,6 +529,7 @@ __global__ __launch_bounds__(kWave) void bucket_quads(SelectArgs a) {
   constexpr int kChunks = kQuadWidth / 4;  // 16-byte chunks per bucket
   constexpr int kLoads = kQuadGroup * kChunks / kWave;  // chunks per lane
   static_assert(kWave / kChunks == 2, "a load covers two buckets");
+  static_assert(KB % 4 == 0, "survivor slots run in chunks of four");
   __shared__ u32x4 stage[kQuadGroup * kStride / 4];
   // The output assembly area at the start of the stage: kOutEntries value
   // words and a spare one, then the indices (bytes or words) from word
@@ -733,14 +734,23 @@ __global__ __launch_bounds__(kWave) void bucket_quads(SelectArgs a) {
         live * kb * static_cast<int>(sizeof(IdxT)), kRsrcWord3);
     // The values of the lane's survivors, lowest column first (the LDS
     // reads issued together rather than one wait per survivor).
+    // Slots run in chunks of four, and a chunk no lane of the wave needs
+    // is skipped (a lane keeps kb / 4 places of its quarter on average).
+    auto chunk_needed = [&](int c4) {
+      return c4 == 0 || __builtin_amdgcn_ballot_w64(count > c4) != 0;
+    };
     uint32_t xs[KB];
     {
       uint32_t k2 = keep;
 #pragma unroll
-      for (int i = 0; i < KB; ++i) {
-        const int c = k2 != 0u ? __builtin_clz(k2) : 0;
-        xs[i] = __float_as_uint(row[c]);
-        k2 &= ~(0x80000000u >> c);
+      for (int c4 = 0; c4 < KB; c4 += 4) {
+        if (!chunk_needed(c4)) break;
+#pragma unroll
+        for (int i = c4; i < c4 + 4; ++i) {
+          const int c = k2 != 0u ? __builtin_clz(k2) : 0;
+          xs[i] = __float_as_uint(row[c]);
+          k2 &= ~(0x80000000u >> c);
+        }
       }
     }
     // The group's outputs are one contiguous stretch of live * kb entries
@@ -756,15 +766,19 @@ __global__ __launch_bounds__(kWave) void bucket_quads(SelectArgs a) {
     asm volatile("" ::: "memory");
     uint32_t* const out_val = reinterpret_cast<uint32_t*>(stage);
 #pragma unroll
-    for (int i = 0; i < KB; ++i) {
-      const int c = keep != 0u ? __builtin_clz(keep) : 0;
-      keep &= ~(0x80000000u >> c);
-      const int e = i < count ? bl * kb + base + i : kOutEntries;
-      out_val[e] = xs[i];
-      if constexpr (sizeof(IdxT) == 1)
-        reinterpret_cast<uint8_t*>(out_val + kOutIdx)[e] = static_cast<uint8_t>(first + c);
-      else
-        out_val[kOutIdx + e] = first + c;
+    for (int c4 = 0; c4 < KB; c4 += 4) {
+      if (!chunk_needed(c4)) break;
+#pragma unroll
+      for (int i = c4; i < c4 + 4; ++i) {
+        const int c = keep != 0u ? __builtin_clz(keep) : 0;
+        keep &= ~(0x80000000u >> c);
+        const int e = i < count ? bl * kb + base + i : kOutEntries;
+        out_val[e] = xs[i];
+        if constexpr (sizeof(IdxT) == 1)
+          reinterpret_cast<uint8_t*>(out_val + kOutIdx)[e] = static_cast<uint8_t>(first + c);
+        else
+          out_val[kOutIdx + e] = first + c;
+      }
     }
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
