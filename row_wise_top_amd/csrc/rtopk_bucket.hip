@@ -495,8 +495,8 @@ __device__ __forceinline__ void merge_top_desc(float (&t)[N], const float (&u)[N
 // 17 KB stage and 64 places per lane) the kernel held 235 registers and ran
 // two waves per SIMD, its vector unit idle half the time (waiting on LDS
 // and permutes); four lanes per bucket halve the stage (16 buckets, 8.4 KB)
-// and the registers (up to four waves per SIMD; the host launches three), at
-// the cost of a second cross-lane merge.
+// and the registers (three waves per SIMD, as many as the host launches),
+// at the cost of a second cross-lane merge.
 
 // A value of lane l and of its partner l ^ D (D = 16 or 32), through the
 // gfx950 lane swaps: lo receives the value of the lane whose bit D is clear,
