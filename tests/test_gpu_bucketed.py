@@ -131,3 +131,41 @@ def test_bucketed_unaligned_outputs(m, k, b, u8):
     assert fv[0].item() == -1.0 and fi[0].item() == 0
     assert_identical((v.cpu().numpy(), i.cpu().numpy().astype(np.int32)),
                      oracle.bucketed(x_np, k, b), f"unaligned outputs m={m} k={k} b={b} u8={u8}")
+
+
+def survivor_layout_rows(n, m, seed, layouts=(0, 1, 2)):
+    """Rows of 128-column buckets whose largest places sit in one quarter
+    (layout 0: one lane of the four-lane kernel keeps them all), four to a
+    quarter (1), or are all equal (2: the lowest columns, hence the first
+    quarter, keep them); the given layouts take turns over the buckets, so
+    that with several one wave of 16 buckets mixes them."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, m)).astype(np.float32)
+    for r in range(n):
+        for j in range(m // 128):
+            bkt = x[r, 128 * j:128 * (j + 1)]
+            layout = layouts[(r * (m // 128) + j) % len(layouts)]
+            if layout == 0:
+                q = (r + j) % 4
+                bkt[32 * q:32 * q + 32] += np.float32(100.0)
+            elif layout == 1:
+                for q in range(4):
+                    bkt[32 * q + rng.choice(32, 4, replace=False)] += np.float32(100.0)
+            else:
+                bkt[:] = np.float32(1.5)
+    return x
+
+
+@pytest.mark.parametrize("layouts", [(0, 1, 2), (1,), (0,), (2,), (1,) * 47 + (0,)])
+@pytest.mark.parametrize("k", [8, 16, 24, 32])
+def test_four_lane_survivor_layouts(k, layouts):
+    # 2 buckets of 128 keeping k / 2 each: the four-lane kernel, whose lanes
+    # run their survivor slots in chunks of four and skip the chunks that no
+    # lane of the wave needs (all of a bucket's survivors in one lane needs
+    # every chunk; four to a quarter in every bucket of a wave only the
+    # first; one one-quarter bucket in 48 makes every third wave of 16
+    # buckets need them all again).
+    x = survivor_layout_rows(1001, 256, 17, layouts)
+    want = oracle.bucketed(x, k, 2)
+    assert_identical(gpu_bucketed(x, k, 2), want, f"layouts {layouts} i32 k={k}")
+    assert_identical(gpu_bucketed(x, k, 2, u8=True), want, f"layouts {layouts} u8 k={k}")
