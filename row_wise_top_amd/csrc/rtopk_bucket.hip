@@ -902,12 +902,13 @@ hipError_t launch_bucket_lanes(const SelectArgs& a, bool u8_index,
     if (hipGetDevice(&device) != hipSuccess) return hipErrorInvalidDevice;
     int per_cu = resident_blocks(reinterpret_cast<const void*>(fn), threads, device);
     if (per_cu >= kSimdsPerCu) per_cu -= per_cu % kSimdsPerCu;
-    // At most three waves per SIMD, though 16 fit: each wave keeps a group
-    // (8 KB) of loads in flight, and fewer of them ran faster (one box, us,
-    // 16 -> 12 waves per CU: 262,144 x 256 in 2 buckets 67.4 -> 66.1, in 8
-    // buckets 58.6 -> 57.9; 1,048,576 x 128, k = 16 135.6 -> 131.9, k = 8
-    // 117.9 -> 116.9; 2,097,152 x 32 58.7 -> 57.9; 8 waves: slower on the
-    // four-lane kernel).
+    // At most three waves per SIMD, though 16 fit at 32 columns (and fitted
+    // the four-lane kernel before its survivor slots ran in chunks): each
+    // wave keeps a group (8 KB) of loads in flight, and fewer of them ran
+    // faster (one box, us, 16 -> 12 waves per CU: 262,144 x 256 in 2
+    // buckets 67.4 -> 66.1, in 8 buckets 58.6 -> 57.9; 1,048,576 x 128,
+    // k = 16 135.6 -> 131.9, k = 8 117.9 -> 116.9; 2,097,152 x 32 58.7 ->
+    // 57.9; 8 waves: slower on the four-lane kernel).
     per_cu = per_cu < kMaxStagedWavesPerCu ? per_cu : kMaxStagedWavesPerCu;
     const int64_t resident = static_cast<int64_t>(cu_count(device)) * per_cu;
     blocks = blocks < resident ? blocks : resident;
